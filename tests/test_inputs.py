@@ -1,0 +1,78 @@
+"""The seeded input generator: rounding, determinism and the long-context key structure (CPU)."""
+
+import numpy as np
+import torch
+
+from transformer_self_attention_amd import inputs
+
+
+def test_bf16_rounding_matches_torch_round_to_nearest_even():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32),
+        (rng.standard_normal(1000) * 1e30).astype(np.float32),
+        (rng.standard_normal(1000) * 1e-30).astype(np.float32),
+        # exact ties between two bf16 values: low 16 bits == 0x8000
+        (np.arange(1, 2000, dtype=np.uint32) << 16 | 0x8000).view(np.float32),
+        np.array([0.0, -0.0, 1.0, -1.0, 65504.0], dtype=np.float32),
+    ])
+    ours = inputs.f32_to_bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ours, ref)
+    back = inputs.bf16_bits_to_f32(ours)
+    assert np.array_equal(back, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+
+
+def test_prefill_draw_is_deterministic_and_ordered():
+    wl = inputs.WORKLOADS["mha"]
+    a = inputs.make_prefill(wl, S=64, B=1)
+    b = inputs.make_prefill(wl, S=64, B=1)
+    assert np.array_equal(a.q.bits, b.q.bits) and np.array_equal(a.v.bits, b.v.bits)
+    # Q, K, V come from one stream in that order
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    q = rng.standard_normal(a.q.f32.size).astype(np.float32)
+    k = rng.standard_normal(a.k.f32.size).astype(np.float32)
+    assert np.array_equal(inputs.f32_to_bf16_bits(q).reshape(a.q.shape), a.q.bits)
+    assert np.array_equal(inputs.f32_to_bf16_bits(k).reshape(a.k.shape), a.k.bits)
+
+
+def test_chunked_draw_equals_single_draw():
+    rng1 = np.random.Generator(np.random.PCG64(5))
+    rng2 = np.random.Generator(np.random.PCG64(5))
+    one = rng1.standard_normal(1000).astype(np.float32)
+    chunked = inputs._normal32(rng2, (1000,), chunk=64)
+    assert np.array_equal(one, chunked)
+
+
+def test_long_context_big_keys_scaled_by_8_exactly():
+    wl = inputs.WORKLOADS["long"]
+    small = inputs.make_prefill(wl, S=2000)
+    nbig = int(round(0.01 * 2000))
+    assert small.big_keys.shape == (1, 8, nbig)
+    # rebuild the unscaled K from the same stream and compare row by row
+    rng = np.random.Generator(np.random.PCG64(wl.seed))
+    _ = rng.standard_normal(1 * 32 * 2000 * 128)
+    k = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(
+        rng.standard_normal(1 * 8 * 2000 * 128).astype(np.float32))).reshape(1, 8, 2000, 128)
+    for h in range(8):
+        big = set(small.big_keys[0, h].tolist())
+        assert len(big) == nbig
+        for j in range(2000):
+            want = k[0, h, j] * (8.0 if j in big else 1.0)
+            assert np.array_equal(small.k.f32[0, h, j], want.astype(np.float32))
+
+
+def test_sampled_rows_include_edges():
+    wl = inputs.WORKLOADS["gqa"]
+    p = inputs.make_prefill(wl, S=1024)
+    assert p.rows.shape == (64, 256)
+    for r in p.rows:
+        assert len(set(r.tolist())) == 256
+        assert {0, 1, 1022, 1023} <= set(r.tolist())
+
+
+def test_workload_work_counts():
+    g = inputs.WORKLOADS["gqa"]
+    assert g.prefill_flops() == 2 * 64 * 8192 ** 2 * 128
+    d = inputs.WORKLOADS["decode"]
+    assert d.decode_kv_bytes() == 1 << 30
