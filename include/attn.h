@@ -1,0 +1,151 @@
+/*
+ * attn.h -- C ABI of libattn.so: rotary position embeddings and exact causal multi-head /
+ * grouped-query scaled dot-product attention for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (all citations name a page and its section):
+ *
+ *   RoPE      "Transformer Architecture & Self-Attention Mechanics" (devthesis.com),
+ *             section 3, "Rotary Position Embeddings (RoPE)": the head vector is cut into
+ *             adjacent pairs (x[2i], x[2i+1]); at position m pair i is turned
+ *             counter-clockwise by m * theta_i, theta_i = base^(-2i/D).
+ *   Attention same page, section 1, the "Attention(Q,K,V)" equation with the row-wise
+ *             softmax; scale 1/sqrt(D).  Causal masking as in the PyTorch listing of
+ *             "Multi-Head Attention & Rotary Position Embeddings (RoPE)"
+ *             (learnllm.online): key j is visible to query i only if j <= i.
+ *   Tiling    "Building Self-Attention and Transformer Engines" (codingpancake.com),
+ *             section 4.1 / 4.2: the S x S score matrix is never written to memory; the
+ *             softmax is accumulated tile by tile with a running max and sum.
+ *   GQA       same page, section 6.1 and the comparison table of section 7: a group of
+ *             G = Hq / Hkv query heads shares one K/V head; query head h reads KV head
+ *             h / G (integer division).
+ *   Decode    "Transformer internals: attention without the mysticism"
+ *             (ninaddeshpande.com), "The KV cache and the memory wall": one new query per
+ *             sequence against the cached keys and values.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensors are dense, row-major ("C order") [B, H, S, D] with D innermost, on the
+ *     device.  Every tensor pointer must be 16-byte aligned.
+ *   - The caller owns all memory.  The library allocates nothing, keeps no state between
+ *     calls, never synchronises, and enqueues its kernels on `stream` (a hipStream_t;
+ *     NULL means the default stream).  Calls are asynchronous: a returned ATTN_OK means
+ *     the work was enqueued.
+ *   - Every argument that can be checked on the host is checked before any HIP call; a
+ *     rejected call enqueues nothing.  HIP launch errors map to ATTN_ERR_HIP.
+ *   - No C++ exception crosses this interface.  Calls are thread-safe (no shared state).
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null pointer, bad size, misalignment, table too short, ... */
+  ATTN_ERR_UNSUPPORTED = 2, /* valid request outside the support matrix (head dim, dtype) */
+  ATTN_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} attn_status;
+
+typedef enum {
+  ATTN_F32 = 0,  /* IEEE binary32 */
+  ATTN_BF16 = 1  /* bfloat16; results are rounded to nearest, ties to even */
+} attn_dtype;
+
+/* Version of this interface (major * 10000 + minor * 100 + patch). */
+int attn_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* attn_status_string(attn_status s);
+
+/* ---------------------------------------------------------------------------------------
+ * RoPE coefficient table.
+ *
+ * Layout: float32 [max_pos][D/2][2]; entry (m, i) holds cos(m * theta_i) then
+ * sin(m * theta_i), theta_i = base^(-2i/D) (devthesis section 3).  The angle m * theta_i
+ * is formed in double precision and its cosine and sine are rounded once to float32.
+ * attn_rope_table_bytes returns the size in bytes (0 if max_pos < 1, D < 2 or D is odd).
+ * attn_rope_table_init fills a caller-allocated device buffer of that size.
+ * Errors: ATTN_ERR_INVALID_ARG for table == NULL, max_pos < 1, odd D or D < 2,
+ * base <= 1, or a table not 16-byte aligned.
+ * --------------------------------------------------------------------------------------- */
+size_t attn_rope_table_bytes(int max_pos, int D);
+attn_status attn_rope_table_init(float* table, int max_pos, int D, double base, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_rope_apply: out[b,h,s,:] = RoPE(x[b,h,s,:]) at position pos0 + s
+ * (devthesis section 3; the dim-8 example of "Transformer Architecture: FlashAttention &
+ * RoPE", academy.kwas.tech).
+ *
+ * x, out: [B, H, S, D] of dtype dt; out == x rotates in place, otherwise the buffers must
+ * not overlap.  The rotation is computed in float32 with the table's coefficients, then
+ * stored as dt.  Any even D >= 2 is accepted.
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers, B/H/S < 1, odd D, pos0 < 0,
+ * pos0 + S > table_max_pos, or misaligned pointers.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int H, int S, int D,
+                            int pos0, const float* rope_table, int table_max_pos, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_prefill: exact attention of S queries against the same S keys, tiled with an
+ * online softmax (codingpancake section 4).
+ *
+ * q: [B, Hq, S, D]; k, v: [B, Hkv, S, D], all of dtype in_dt.
+ * o: [B, Hq, S, D] of dtype out_dt (written in full).
+ * lse: optional float32 [B, Hq, S]; if not NULL receives the natural-log normaliser
+ *      m + ln(sum_j exp(s_ij - m)) of the scaled scores of each row.
+ * rope_table: NULL disables RoPE; otherwise Q and K rows are rotated at positions
+ *      pos0 + s before the product (V is never rotated); requires pos0 >= 0 and
+ *      pos0 + S <= table_max_pos.
+ * causal != 0 masks key j > query i (square mask anchored at the top-left); causal == 0
+ *      lets every query see every key.
+ * Scale: 1/sqrt(D), fixed.
+ *
+ * Support matrix: D in {64, 128}; in_dt = ATTN_F32 (float32 arithmetic throughout, out_dt
+ * must be ATTN_F32) or in_dt = ATTN_BF16 (out_dt either).  For bf16 input the rotated
+ * q and k are rounded to IEEE half precision for the Q.K^T matrix-core product (fp32
+ * accumulation), so |q|, |k| must stay below 4.6e4; the softmax weights are rounded to
+ * bf16 for the P.V product (fp32 accumulation).
+ * Errors: ATTN_ERR_INVALID_ARG for null q/k/v/o, B/Hq/Hkv/S < 1, Hq % Hkv != 0, bad RoPE
+ * range, misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
+                         int causal, int pos0, const float* rope_table, int table_max_pos,
+                         void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV
+ * cache and the memory wall"), split over the cache length ("split-K") with a merge pass.
+ *
+ * q: [B, Hq, 1, D] (not yet rotated); k_cache, v_cache: [B, Hkv, S_max, D], keys already
+ * rotated (used exactly as stored); all of dtype in_dt.
+ * cache_len, q_pos: device int32 [B].  Sequence b attends to cache rows
+ * [0, min(cache_len[b], S_max)); its query is rotated at position q_pos[b] (if rope_table
+ * is not NULL).  A row with cache_len[b] <= 0 yields o = 0 and lse = -inf.  A row whose
+ * q_pos[b] lies outside [0, table_max_pos) yields NaN (the table has no such row).
+ * o: [B, Hq, 1, D] of dtype out_dt; lse: optional float32 [B, Hq].
+ * n_split: number of cache chunks per (sequence, KV head); 0 picks one from the shape.
+ * workspace: device scratch of at least attn_decode_workspace_bytes(...) bytes with the
+ * same B, Hq, Hkv, S_max, D and n_split; its contents on entry do not matter.
+ *
+ * Support matrix: in_dt = ATTN_BF16, D in {64, 128}, out_dt either.
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers, sizes < 1, Hq % Hkv != 0, n_split < 0,
+ * workspace too small, misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * --------------------------------------------------------------------------------------- */
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D, int n_split);
+int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split);
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                        attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
+                        int D, const float* rope_table, int table_max_pos, int n_split,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

@@ -1,0 +1,132 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects bad
+arguments on the host with the documented status code before touching any device."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from transformer_self_attention_amd import lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+P = ctypes.c_void_p
+A = P(0x10000)          # 16-byte aligned fake device address (never dereferenced on these paths)
+MIS = P(0x10008)        # 8-byte aligned only
+OK, INV, UNSUP = lib.ATTN_OK, lib.ATTN_ERR_INVALID_ARG, lib.ATTN_ERR_UNSUPPORTED
+F32, BF16 = lib.ATTN_F32, lib.ATTN_BF16
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = declared_functions()
+    assert len(names) >= 9
+    raw = lib.raw()
+    for n in names:
+        assert hasattr(raw, n), n
+    assert set(names) == set(lib.EXPORTED)
+
+
+def test_version_and_status_strings():
+    assert lib.version() == 10000
+    assert lib.status_string(OK) == "ATTN_OK"
+    for s in (INV, UNSUP, lib.ATTN_ERR_HIP):
+        assert lib.status_string(s).startswith("ATTN_ERR_")
+    assert lib.status_string(99) == "unknown attn_status"
+
+
+def test_rope_table_bytes():
+    assert lib.rope_table_bytes(8192, 128) == 8192 * 128 * 4
+    assert lib.rope_table_bytes(1, 2) == 8
+    for bad in ((0, 128), (10, 7), (10, 0), (-1, 64)):
+        assert lib.rope_table_bytes(*bad) == 0
+
+
+def _prefill(**kw):
+    a = dict(q=A, k=A, v=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=1, Hq=8, Hkv=2, S=100, D=128,
+             causal=1, pos0=0, table=A, tmax=100, stream=None)
+    a.update(kw)
+    return lib.raw().attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["in_dt"], a["out_dt"], a["B"],
+                                  a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["pos0"], a["table"],
+                                  a["tmax"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(k=None), INV), (dict(v=None), INV), (dict(o=None), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV), (dict(S=0), INV), (dict(D=0), INV),
+    (dict(Hq=8, Hkv=3), INV), (dict(q=MIS), INV), (dict(o=MIS), INV), (dict(lse=MIS), INV),
+    (dict(tmax=99), INV), (dict(pos0=-1), INV), (dict(pos0=1), INV), (dict(table=MIS), INV),
+    (dict(D=65), INV), (dict(in_dt=7), INV), (dict(out_dt=-1), INV),
+    (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP), (dict(in_dt=F32, out_dt=BF16), UNSUP),
+    (dict(D=96, table=None), UNSUP),
+])
+def test_prefill_rejects(kw, code):
+    assert _prefill(**kw) == code
+
+
+def _decode(**kw):
+    a = dict(q=A, kc=A, vc=A, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=4, Hq=16, Hkv=2,
+             S=1000, D=128, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], max(a["S"], 1), max(a["D"], 1),
+                                              max(a["ns"], 0))
+    return lib.raw().attn_decode(a["q"], a["kc"], a["vc"], a["cl"], a["qp"], a["o"], a["lse"], a["in_dt"],
+                                 a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["table"], a["tmax"],
+                                 a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kc=None), INV), (dict(vc=None), INV), (dict(cl=None), INV),
+    (dict(o=None), INV), (dict(ws=None), INV), (dict(qp=None), INV),
+    (dict(B=0), INV), (dict(Hq=15), INV), (dict(S=0), INV), (dict(ns=-1), INV),
+    (dict(wsb=16), INV), (dict(kc=MIS), INV), (dict(ws=MIS), INV), (dict(cl=P(0x10002)), INV),
+    (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
+    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+])
+def test_decode_rejects(kw, code):
+    assert _decode(**kw) == code
+
+
+def test_rope_apply_rejects():
+    raw = lib.raw()
+    call = lambda x=A, out=A, dt=BF16, B=1, H=2, S=10, D=8, pos0=0, table=A, tmax=10: raw.attn_rope_apply(
+        x, out, dt, B, H, S, D, pos0, table, tmax, None)
+    assert call(x=None) == INV
+    assert call(out=None) == INV
+    assert call(table=None) == INV
+    assert call(D=7) == INV
+    assert call(S=0) == INV
+    assert call(pos0=1) == INV          # pos0 + S > table rows
+    assert call(x=MIS) == INV
+    assert call(dt=3) == INV
+
+
+def test_rope_table_init_rejects():
+    raw = lib.raw()
+    assert raw.attn_rope_table_init(None, 10, 8, 10000.0, None) == INV
+    assert raw.attn_rope_table_init(A, 0, 8, 10000.0, None) == INV
+    assert raw.attn_rope_table_init(A, 10, 7, 10000.0, None) == INV
+    assert raw.attn_rope_table_init(A, 10, 8, 1.0, None) == INV
+    assert raw.attn_rope_table_init(A, 10, 8, float("nan"), None) == INV
+    assert raw.attn_rope_table_init(MIS, 10, 8, 10000.0, None) == INV
+
+
+def test_decode_workspace_geometry():
+    B, Hq, Hkv, S, D = 32, 64, 8, 8192, 128
+    ns = lib.decode_num_splits(B, Hq, Hkv, S, D, 0)
+    assert ns == 8                     # 256 (sequence, KV head) units x 8 splits = 2048 workgroups
+    assert lib.decode_workspace_bytes(B, Hq, Hkv, S, D, 0) == B * Hq * ns * (D + 2) * 4
+    # explicit split counts are honoured up to whole 32-key chunks
+    assert lib.decode_num_splits(1, 8, 1, 200, 64, 3) == 3   # 67 keys -> 96-key chunks
+    assert lib.decode_num_splits(1, 8, 1, 100, 64, 3) == 2   # 34 keys -> 64-key chunks
+    assert lib.decode_num_splits(1, 8, 1, 40, 64, 8) == 2
+    assert lib.decode_num_splits(1, 8, 1, 1, 64, 0) == 1
+    assert lib.decode_workspace_bytes(0, 8, 1, 100, 64, 0) == 0

@@ -1,0 +1,173 @@
+// C ABI of libattn.so (declared in include/attn.h): argument validation and kernel dispatch.
+//
+// Every check that can run on the host runs before the first HIP call, so a rejected call
+// enqueues nothing and touches no device state.
+#include "../../include/attn.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "common.h"
+
+namespace {
+
+constexpr int kVersion = 10000;  // 1.0.0
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP; }
+
+inline bool valid_dtype(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
+
+attn_status check_rope(const float* table, int table_max_pos, int pos0, int S) {
+  if (!table) return ATTN_OK;
+  if (!aligned16(table) || table_max_pos < 1 || pos0 < 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)pos0 + S > (int64_t)table_max_pos) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Decode split geometry: keys per split are a multiple of the 32-key wave block.
+void decode_geometry(int B, int Hkv, int S_max, int n_split_req, int* n_split, int* chunk) {
+  int ns = n_split_req;
+  if (ns <= 0) {
+    // Aim for >= 2048 workgroups (8 per CU) while keeping >= 256 keys per split.
+    const int64_t units = (int64_t)B * Hkv;
+    int64_t want = (2048 + units - 1) / units;
+    int64_t cap = S_max / 256;
+    if (cap < 1) cap = 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    ns = (int)want;
+  }
+  int c = (S_max + ns - 1) / ns;
+  c = ((c + 31) / 32) * 32;
+  if (c < 32) c = 32;
+  // drop splits that would start past S_max
+  int ns_eff = (S_max + c - 1) / c;
+  if (ns_eff < 1) ns_eff = 1;
+  *n_split = ns_eff;
+  *chunk = c;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_version(void) { return kVersion; }
+
+const char* attn_status_string(attn_status s) {
+  switch (s) {
+    case ATTN_OK: return "ATTN_OK";
+    case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
+    case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: outside the support matrix";
+    case ATTN_ERR_HIP: return "ATTN_ERR_HIP: HIP runtime error at launch";
+  }
+  return "unknown attn_status";
+}
+
+size_t attn_rope_table_bytes(int max_pos, int D) {
+  if (max_pos < 1 || D < 2 || (D & 1)) return 0;
+  return (size_t)max_pos * (size_t)D * sizeof(float);
+}
+
+attn_status attn_rope_table_init(float* table, int max_pos, int D, double base, void* stream) {
+  if (!table || !aligned16(table) || max_pos < 1 || D < 2 || (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!(base > 1.0) || !std::isfinite(base)) return ATTN_ERR_INVALID_ARG;
+  return from_hip(attn::launch_rope_table(table, max_pos, D, base, (hipStream_t)stream));
+}
+
+attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int H, int S, int D,
+                            int pos0, const float* rope_table, int table_max_pos, void* stream) {
+  if (!x || !out || !rope_table) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || S < 1 || D < 2 || (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(out)) return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const int64_t rows = (int64_t)B * H * S;
+  return from_hip(attn::launch_rope_apply(x, out, dt == ATTN_BF16, rows, S, D, pos0, rope_table,
+                                          (hipStream_t)stream));
+}
+
+attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
+                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
+                         int causal, int pos0, const float* rope_table, int table_max_pos,
+                         void* stream) {
+  if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (in_dt == ATTN_F32 && out_dt != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * S > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+
+  attn::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+  a.causal = causal != 0;
+  a.pos0 = pos0;
+  a.table = rope_table;
+  hipStream_t st = (hipStream_t)stream;
+  return from_hip(in_dt == ATTN_F32 ? attn::launch_prefill_f32(a, st) : attn::launch_prefill_bf16(a, st));
+}
+
+int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {
+  (void)Hq; (void)D;
+  if (B < 1 || Hkv < 1 || S_max < 1 || n_split < 0) return 0;
+  int ns, chunk;
+  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  return ns;
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D, int n_split) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return 0;
+  int ns, chunk;
+  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  const size_t parts = (size_t)B * Hq * ns;
+  return parts * (size_t)D * sizeof(float) + parts * 2 * sizeof(float);
+}
+
+attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                        const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                        attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
+                        int D, const float* rope_table, int table_max_pos, int n_split,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !cache_len || !o || !workspace) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && !q_pos) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      !aligned16(workspace) || (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) ||
+      (q_pos && (reinterpret_cast<uintptr_t>(q_pos) & 3u)))
+    return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (!aligned16(rope_table) || table_max_pos < 1)) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split))
+    return ATTN_ERR_INVALID_ARG;
+  if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * S_max * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+
+  int ns, chunk;
+  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  attn::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache;
+  a.cache_len = cache_len; a.q_pos = q_pos;
+  a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_max = S_max; a.D = D;
+  a.table = rope_table; a.table_max_pos = table_max_pos;
+  a.n_split = ns; a.chunk = chunk;
+  const size_t parts = (size_t)B * Hq * ns;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = static_cast<float*>(workspace) + parts * D;
+  return from_hip(attn::launch_decode(a, (hipStream_t)stream));
+}
+
+}  // extern "C"

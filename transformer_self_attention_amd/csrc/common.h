@@ -1,0 +1,97 @@
+// Internal declarations shared by the HIP sources of libattn.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define ATTN_LDS __attribute__((address_space(3)))
+
+// bfloat16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> two packed bfloat16 (round to nearest even; v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Two floats -> two packed IEEE halves (round to nearest even).
+__device__ __forceinline__ uint32_t pack_f16(float a, float b) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  f16x2 v;
+  v[0] = (_Float16)a;
+  v[1] = (_Float16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Value of lane (l xor 32) for every lane l, via v_permlane32_swap.
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  const bool upper = (threadIdx.x & 32) != 0;
+  return __uint_as_float(upper ? r[0] : r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ------------------------------------------------------------------------------------------
+// Launchers (each returns hipGetLastError() of its launch).  Arguments were validated by the
+// C-ABI layer; the launchers only size grids.
+// ------------------------------------------------------------------------------------------
+hipError_t launch_rope_table(float* table, int max_pos, int D, double base, hipStream_t st);
+
+hipError_t launch_rope_apply(const void* x, void* out, bool bf16, int64_t rows, int S, int D,
+                             int pos0, const float* table, hipStream_t st);
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  bool out_bf16;
+  int B, Hq, Hkv, S, D;
+  bool causal;
+  int pos0;
+  const float* table;  // nullptr: no RoPE
+};
+
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cache_len;
+  const int32_t* q_pos;
+  void* o;
+  float* lse;
+  bool out_bf16;
+  int B, Hq, Hkv, S_max, D;
+  const float* table;  // nullptr: no RoPE
+  int table_max_pos;
+  int n_split;
+  int chunk;           // keys per split (multiple of the kernel's key block)
+  float* ws_o;         // [B, Hq, n_split, D]
+  float* ws_ml;        // [B, Hq, n_split, 2]
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
+
+}  // namespace attn

@@ -1,0 +1,327 @@
+// Decode: one new query per sequence against a KV cache, split over the cache ("split-K"),
+// followed by a merge pass.
+//
+// Method: the KV-cache decode step of ninaddeshpande.com "Transformer internals: attention
+// without the mysticism" ("The KV cache and the memory wall"): each query row attends to every
+// cached key; the cache holds already-rotated keys and is used as stored, the query is rotated
+// (devthesis.com section 3) at its own position.  The G = Hq/Hkv query heads that share a KV head
+// (codingpancake.com section 6.1) are processed together so each K/V byte is read once.
+//
+// Pass 1 (decode_split_kernel), one workgroup per (sequence, KV head, split):
+//  * 4 waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
+//    flight while sub-block i is consumed (16 x 16-byte loads per lane).
+//  * Scores S^T = K q^T on v_mfma_f32_16x16x32_bf16: K goes from HBM straight into the A
+//    operand; the G query rows (padded to 16) form the B operand.  The rotated, scaled query is
+//    split into bf16 hi + lo parts and multiplied twice, so q keeps ~16 significant bits and K is
+//    used exactly.  The matrix cores are nearly idle in this memory-bound pass.
+//  * Online softmax per row in log2 units (row max over the 4 lane groups with permlane swaps),
+//    lazy rescaling as in prefill.
+//  * O^T += V^T P^T on the same MFMA shape; V^T comes from a wave-private LDS tile through
+//    ds_read_b64_tr_b16.
+//  * The 4 waves' (m, l, O) are merged through LDS and one partial per (row, split) is written.
+// Pass 2 (decode_merge_kernel), one workgroup per (sequence, query head): combines the splits
+// with the same log-sum-exp algebra and writes o and lse.
+#include "common.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kSub = 32;   // keys per wave iteration
+constexpr float kRescaleThreshold = 8.0f;
+
+// max / sum partners across the 16-lane rows of a wave.
+__device__ __forceinline__ float max_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ int vswz(int r, int lc) {  // 16 chunks per row (D = 128)
+  return lc ^ (((r & 3) << 2) | ((r >> 2) & 3));
+}
+
+template <int D, bool ROPE>
+__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int Hq, int Hkv,
+    int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
+    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+  constexpr int NCH = D / 8;
+  constexpr int KS = D / 32;        // MFMA k-steps over D
+  constexpr int DB = D / 16;        // 16-wide output blocks over D
+  constexpr int LPT = kSub * NCH / 64;  // 16-byte loads of K (and of V) per lane per sub-block
+  static_assert(D == 128 || D == 64, "head dim");
+
+  // Per-wave V tile; after the key loop each wave reuses its own tile (same bytes) to publish
+  // its O^T for the cross-wave merge: 16 rows x D floats == 32 keys x D bf16.
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kWaves][kSub * D];
+  __shared__ float red_ml[kWaves][16][2];
+
+  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int qrow = i16;  // this lane's query row in the group (B-operand column / C column)
+
+  int L = cache_len[b];
+  L = L < 0 ? 0 : (L > S_max ? S_max : L);
+  const int kbeg = split * chunk;
+  const int kend = min(kbeg + chunk, L);
+
+  // ---- query fragments (hi/lo bf16), rotated at q_pos[b] and scaled by log2(e)/sqrt(D) ----
+  bf16x8 qhi[KS], qlo[KS];
+  {
+    const float qscale = 1.4426950408889634f / sqrtf((float)D);
+    int pos = 0;
+    if constexpr (ROPE) {
+      pos = q_pos[b];
+      if (pos < 0 || pos >= table_max_pos) pos = 0;  // the merge pass reports such rows as NaN
+    }
+    const bool valid = qrow < G;
+    const uint16_t* qp = q + ((int64_t)b * Hq + hkv * G + (valid ? qrow : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 32 * ks + 8 * g16;
+      u32x4 w = *reinterpret_cast<const u32x4*>(qp + d0);
+      if (!valid) w = u32x4{0, 0, 0, 0};
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
+      if constexpr (ROPE) {
+        const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)pos * (D / 2) + d0 / 2);
+        const f32x4 c01 = tp[0], c23 = tp[1];
+        const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float c = cs[2 * p], s = cs[2 * p + 1];
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * c - x1 * s;
+          x[2 * p + 1] = x0 * s + x1 * c;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        const float xs = x[t] * qscale;
+        const __bf16 hi = (__bf16)xs;
+        qhi[ks][t] = hi;
+        qlo[ks][t] = (__bf16)(xs - (float)hi);
+      }
+    }
+  }
+
+  const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S_max * D;
+  const uint16_t* kg = kc + kv_off;
+  const uint16_t* vg = vc + kv_off;
+
+  f32x4 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // K: lane loads key (kb*16 + i16), 16 B at d = 32 ks + 8 g16  -> A operand directly.
+  // V: lane loads chunk c = lane + 64 i of the 32 x D tile (row c / NCH, chunk c % NCH).
+  u32x4 kst[2][KS], vst[LPT];
+  auto issue = [&](int k0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = k0 + kb * 16 + i16;
+      const bool ok = key < kend;
+      const uint16_t* kp = kg + (int64_t)(ok ? key : kbeg) * D + 8 * g16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kst[kb][ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = lane + 64 * i;
+      const int key = k0 + c / NCH;
+      const bool ok = key < kend;
+      vst[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)(ok ? key : kbeg) * D + (c % NCH) * 8);
+      if (!ok) vst[i] = u32x4{0, 0, 0, 0};
+    }
+  };
+
+  ATTN_LDS uint16_t* vl = (ATTN_LDS uint16_t*)(v_lds[wave]);
+  const int nsub = kend > kbeg ? (kend - kbeg + kSub - 1) / kSub : 0;
+  int it = wave;
+  if (it < nsub) issue(kbeg + it * kSub);
+  for (; it < nsub; it += kWaves) {
+    const int k0 = kbeg + it * kSub;
+    // consume staged registers
+    u32x4 kcur[2][KS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) kcur[kb][ks] = kst[kb][ks];
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int c = lane + 64 * i;
+      const int r = c / NCH, cc = c % NCH;
+      const int off = r * D + (D == 128 ? vswz(r, cc) : (cc ^ (r & 7))) * 8;
+      *reinterpret_cast<ATTN_LDS u32x4*>(vl + off) = vst[i];
+    }
+    if (it + kWaves < nsub) issue(k0 + kWaves * kSub);
+
+    // scores
+    f32x4 sacc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      sacc[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = __builtin_bit_cast(bf16x8, kcur[kb][ks]);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qhi[ks], sacc[kb], 0, 0, 0);
+        sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[ks], sacc[kb], 0, 0, 0);
+      }
+    }
+    if (k0 + kSub > kend) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (k0 + kb * 16 + 4 * g16 + r >= kend) sacc[kb][r] = -INFINITY;
+    }
+    float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
+                     fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
+    mx = max_xor16(mx);
+    mx = max_xor32(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleThreshold) != 0) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < DB; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pf;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const float p = fast_exp2(sacc[t >> 2][t & 3] - m_run);
+      l_run += p;
+      pf[t] = (__bf16)p;
+    }
+    // O^T += V^T P^T ; key order inside the contraction: t -> (t/4)*16 + 4*g16 + t%4
+#pragma unroll
+    for (int db = 0; db < DB; ++db) {
+      bf16x8 a;
+#pragma unroll
+      for (int tg = 0; tg < 2; ++tg) {
+        const int vr = tg * 16 + 4 * g16 + (i16 >> 2);
+        const int lc = 2 * db + ((i16 & 3) >> 1);
+        const int off = vr * D + (D == 128 ? vswz(vr, lc) : (lc ^ (vr & 7))) * 8 + 4 * (i16 & 1);
+        const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(reinterpret_cast<ATTN_LDS i16x4*>(vl + off));
+        const bf16x4 wb = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) a[4 * tg + e] = wb[e];
+      }
+      oacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, oacc[db], 0, 0, 0);
+    }
+  }
+
+  // ---- combine the 4 waves ----
+  l_run = sum_xor32(sum_xor16(l_run));
+  if (lane < 16) {
+    red_ml[wave][qrow][0] = m_run;
+    red_ml[wave][qrow][1] = l_run;
+  }
+  ATTN_LDS float* red_o = (ATTN_LDS float*)(&v_lds[0][0]);  // [wave][16][D]
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_o[(wave * 16 + qrow) * D + db * 16 + 4 * g16 + r] = oacc[db][r];
+  __syncthreads();
+
+  // thread -> (row, d) pairs of the merged partial
+  for (int e = tid; e < G * D; e += kThreads) {
+    const int rr = e / D, d = e % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][rr][0]);
+    float Lsum = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(red_ml[w][rr][0] - M);
+        Lsum += red_ml[w][rr][1] * sc;
+        acc += red_o[(w * 16 + rr) * D + d] * sc;
+      }
+    }
+    const int64_t part = (((int64_t)b * Hq + hkv * G + rr) * n_split + split);
+    ws_o[part * D + d] = acc;
+    if (d == 0) {
+      ws_ml[part * 2 + 0] = M;
+      ws_ml[part * 2 + 1] = Lsum;
+    }
+  }
+}
+
+template <int D, bool OUT_BF16, bool ROPE>
+__global__ __launch_bounds__(D) void decode_merge_kernel(
+    const float* __restrict__ ws_o, const float* __restrict__ ws_ml, const int32_t* __restrict__ q_pos,
+    int table_max_pos, int Hq, int n_split, void* __restrict__ o, float* __restrict__ lse) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int64_t base = ((int64_t)b * Hq + h) * n_split;
+  float M = -INFINITY;
+  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ws_ml[(base + s) * 2]);
+  float Lsum = 0.f, acc = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < n_split; ++s) {
+      const float sc = fast_exp2(ws_ml[(base + s) * 2] - M);
+      Lsum += ws_ml[(base + s) * 2 + 1] * sc;
+      acc += ws_o[(base + s) * D + d] * sc;
+    }
+  }
+  float out = Lsum > 0.f ? acc / Lsum : 0.f;
+  float ls = Lsum > 0.f ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
+  if constexpr (ROPE) {
+    const int p = q_pos[b];
+    if (p < 0 || p >= table_max_pos) { out = __builtin_nanf(""); ls = __builtin_nanf(""); }
+  }
+  const int64_t oi = ((int64_t)b * Hq + h) * D + d;
+  if constexpr (OUT_BF16) {
+    reinterpret_cast<__bf16*>(o)[oi] = (__bf16)out;
+  } else {
+    reinterpret_cast<float*>(o)[oi] = out;
+  }
+  if (lse && d == 0) lse[(int64_t)b * Hq + h] = ls;
+}
+
+template <int D, bool ROPE>
+hipError_t go(const DecodeArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((decode_split_kernel<D, ROPE>), dim3(a.n_split, a.Hkv, a.B), dim3(kThreads), 0, st,
+                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cache_len,
+                     a.q_pos, a.Hq, a.Hkv, a.S_max, reinterpret_cast<const float2*>(a.table),
+                     a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (a.out_bf16)
+    hipLaunchKernelGGL((decode_merge_kernel<D, true, ROPE>), dim3(a.Hq, a.B), dim3(D), 0, st, a.ws_o,
+                       a.ws_ml, a.q_pos, a.table_max_pos, a.Hq, a.n_split, a.o, a.lse);
+  else
+    hipLaunchKernelGGL((decode_merge_kernel<D, false, ROPE>), dim3(a.Hq, a.B), dim3(D), 0, st, a.ws_o,
+                       a.ws_ml, a.q_pos, a.table_max_pos, a.Hq, a.n_split, a.o, a.lse);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
+  const bool rope = a.table != nullptr;
+  if (a.D == 64) return rope ? go<64, true>(a, st) : go<64, false>(a, st);
+  return rope ? go<128, true>(a, st) : go<128, false>(a, st);
+}
+
+}  // namespace attn

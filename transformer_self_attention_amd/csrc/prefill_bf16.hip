@@ -1,0 +1,349 @@
+// bf16 prefill on the gfx950 matrix cores: exact attention tiled with an online softmax.
+//
+// Method: scaled dot-product attention, devthesis.com "Transformer Architecture & Self-Attention
+// Mechanics" section 1; causal mask of the learnllm.online listing; RoPE of devthesis section 3
+// fused into the Q and K tile loads; the tiling with a running row max and row sum of
+// codingpancake.com "Building Self-Attention and Transformer Engines" sections 4.1-4.2 (the score
+// tile never leaves registers); GQA head sharing of the same page, section 6.1.
+//
+// Shape of the kernel (one workgroup = 4 waves = 128 query rows of one head):
+//  * Each wave owns 32 query rows.  Its rotated Q (scaled by log2(e)/sqrt(D), fp16) sits in
+//    registers as the B operand of v_mfma_f32_32x32x16_f16.
+//  * Keys arrive in tiles of 64, double-buffered in LDS: K rotated in fp32 and stored as fp16,
+//    V stored as bf16, both with an XOR swizzle of 16-byte chunks so that the MFMA operand reads
+//    are bank-conflict free.
+//  * Scores are computed transposed, S^T = K Q^T, so that each lane holds 32 scores of ONE
+//    query row (the other 32 of the tile sit in lane l^32): the row max is a local max3 tree
+//    plus one v_permlane32_swap; the row sum stays lane-local until the end.
+//  * P (bf16) is consumed straight from those registers as the B operand of the P.V product
+//    O^T += V^T P^T; the V^T operand comes from LDS through ds_read_b64_tr_b16.  The key order
+//    inside the contraction is permuted so that no register shuffle is needed.
+//  * Online softmax in log2 units with lazy rescaling: O and l are rescaled only when a row's
+//    max grows by more than 8 (so unnormalised weights stay <= 2^8); the result is the same
+//    softmax, normalised once at the end.
+//  * Causal: tiles entirely above a wave's rows are skipped; only tiles crossing the diagonal
+//    (or the tail S) are masked.
+//  * Workgroup order: heaviest query blocks first; the G query heads sharing one KV head (and
+//    the same query block) are sent to the same XCD so its L2 serves their K/V reads.
+#include "common.h"
+
+namespace attn {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kRowsPerWave = 32;
+constexpr int kBM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kBN = 64;                     // keys per tile
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr int kNumXcd = 8;
+
+// Physical 16-byte chunk of logical chunk `lc` in LDS row `r`.
+template <int D>
+__device__ __forceinline__ int swz(int r, int lc) {
+  if constexpr (D == 128) {
+    return lc ^ (((r & 3) << 2) | ((r >> 2) & 3));
+  } else {
+    return lc ^ (r & 7);
+  }
+}
+
+template <int D, bool CAUSAL, bool ROPE, bool OUT_BF16>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                         const uint16_t* __restrict__ v, void* __restrict__ o,
+                         float* __restrict__ lse, int B, int Hq, int Hkv, int S, int pos0,
+                         const float2* __restrict__ table) {
+  constexpr int NCH = D / 8;                 // 16-byte chunks per row
+  constexpr int KS = D / 16;                 // MFMA k-steps over D
+  constexpr int DB = D / 32;                 // 32-wide output blocks over D
+  constexpr int CPT = kBN * NCH / kThreads;  // chunks of K (and of V) per thread per tile
+  constexpr int TILE_ELEMS = kBN * D;
+
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TILE_ELEMS];
+
+  // ---- workgroup -> (query block, batch, head) ----
+  const int G = Hq / Hkv;
+  const int nqb = (S + kBM - 1) / kBM;
+  const int NG = nqb * B * Hkv;
+  const int id = blockIdx.x;
+  const int xcd = id % kNumXcd;
+  const int j = id / kNumXcd;
+  const int gi = (j / G) * kNumXcd + xcd;
+  if (gi >= NG) return;
+  const int gq = j % G;
+  const int qblock = CAUSAL ? (nqb - 1 - gi / (B * Hkv)) : (gi / (B * Hkv));
+  const int rem = gi % (B * Hkv);
+  const int b = rem / Hkv;
+  const int hkv = rem % Hkv;
+  const int h = hkv * G + gq;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int hl = lane >> 5;      // which half of the wave
+  const int l32 = lane & 31;
+  const int q0 = qblock * kBM;
+  const int qw = q0 + wave * kRowsPerWave;  // first row of this wave
+  const int row = qw + l32;                 // this lane's query row
+  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+
+  // ---- Q: load, rotate, scale, convert to fp16 B-operand fragments ----
+  f16x8 qf[KS];
+  {
+    const int rc = row < S ? row : S - 1;
+    const uint16_t* qrow = q + (((int64_t)b * Hq + h) * S + rc) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 16 * ks + 8 * hl;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
+      if constexpr (ROPE) {
+        const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + rc) * (D / 2) + d0 / 2);
+        const f32x4 c01 = tp[0], c23 = tp[1];
+        const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float c = cs[2 * p], s = cs[2 * p + 1];
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * c - x1 * s;
+          x[2 * p + 1] = x0 * s + x1 * c;
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * qscale);
+    }
+  }
+
+  // ---- key range ----
+  const int q_last = min(q0 + kBM, S) - 1;
+  const int key_end = CAUSAL ? q_last + 1 : S;
+  const int n_tiles = (key_end + kBN - 1) / kBN;
+  const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S * D;
+  const uint16_t* kg = k + kv_off;
+  const uint16_t* vg = v + kv_off;
+
+  // staging registers for one tile
+  u32x4 kst[CPT], vst[CPT];
+  f32x4 tst[CPT][2];
+  auto issue_loads = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / NCH, cc = c % NCH;
+      const int key = k0 + r;
+      if (key < S) {
+        kst[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * D + cc * 8);
+        vst[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * D + cc * 8);
+        if constexpr (ROPE) {
+          const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + key) * (D / 2) + cc * 4);
+          tst[i][0] = tp[0];
+          tst[i][1] = tp[1];
+        }
+      } else {
+        kst[i] = u32x4{0, 0, 0, 0};
+        vst[i] = u32x4{0, 0, 0, 0};
+        if constexpr (ROPE) {
+          tst[i][0] = f32x4{1.f, 0.f, 1.f, 0.f};
+          tst[i][1] = f32x4{1.f, 0.f, 1.f, 0.f};
+        }
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + kThreads * i;
+      const int r = c / NCH, cc = c % NCH;
+      float x[8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(kst[i][t]); x[2 * t + 1] = bf16hi(kst[i][t]); }
+      if constexpr (ROPE) {
+        const float cs[8] = {tst[i][0][0], tst[i][0][1], tst[i][0][2], tst[i][0][3],
+                             tst[i][1][0], tst[i][1][1], tst[i][1][2], tst[i][1][3]};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float c = cs[2 * p], s = cs[2 * p + 1];
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * c - x1 * s;
+          x[2 * p + 1] = x0 * s + x1 * c;
+        }
+      }
+      u32x4 kh;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kh[t] = pack_f16(x[2 * t], x[2 * t + 1]);
+      const int off = r * D + swz<D>(r, cc) * 8;
+      *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_lds[buf]) + off) = kh;
+      *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(v_lds[buf]) + off) = vst[i];
+    }
+  };
+
+  // ---- accumulators ----
+  f32x16 oacc[DB];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;
+  float l_run = 0.f;
+
+  // per-lane LDS read geometry
+  const int g16 = lane >> 4;     // 16-lane group
+  const int i16 = lane & 15;
+
+  issue_loads(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    const int k0 = t * kBN;
+    store_tile(buf);
+    __syncthreads();
+    if (t + 1 < n_tiles) issue_loads(k0 + kBN);
+
+    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
+      const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_lds[buf]);
+      const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_lds[buf]);
+      // S^T = K Q^T for two 32-key blocks
+      f32x16 sacc[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        const int kr = kb * 32 + l32;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int off = kr * D + swz<D>(kr, 2 * ks + hl) * 8;
+          const f16x8 a = *reinterpret_cast<const ATTN_LDS f16x8*>(kb_lds + off);
+          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], sacc[kb], 0, 0, 0);
+        }
+      }
+      // mask (diagonal / tail tiles only)
+      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw) || (k0 + kBN > S);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if ((CAUSAL && key > row) || key >= S) sacc[kb][r] = -INFINITY;
+          }
+      }
+      // row max over this tile
+      float mx = sacc[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = fast_exp2(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        m_run = m_new;
+      }
+      // p = 2^(s - m), packed to bf16 as the B operand of P.V
+      bf16x8 pf[2][2];
+      float lsum = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          float p[8];
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) {
+            p[tt] = fast_exp2(sacc[kb][8 * s + tt] - m_run);
+            lsum += p[tt];
+          }
+#pragma unroll
+          for (int tt = 0; tt < 8; ++tt) pf[kb][s][tt] = (__bf16)p[tt];
+        }
+      l_run += lsum;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            bf16x8 a;
+#pragma unroll
+            for (int tg = 0; tg < 2; ++tg) {
+              const int vr = kb * 32 + 16 * s + 8 * tg + 4 * hl + (i16 >> 2);
+              const int lc = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+              const int off = vr * D + swz<D>(vr, lc) * 8 + 4 * (i16 & 1);
+              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                  reinterpret_cast<ATTN_LDS i16x4*>(const_cast<ATTN_LDS uint16_t*>(vb_lds) + off));
+              const bf16x4 wb = __builtin_bit_cast(bf16x4, w);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) a[4 * tg + e] = wb[e];
+            }
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][s], oacc[db], 0, 0, 0);
+          }
+    }
+  }
+
+  // ---- finalize ----
+  const float l_tot = l_run + swap_halves(l_run);
+  if (row < S) {
+    const float inv = 1.0f / l_tot;
+    const int64_t orow = (((int64_t)b * Hq + h) * S + row) * D;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * hl;
+        const float o0 = oacc[db][4 * r4 + 0] * inv, o1 = oacc[db][4 * r4 + 1] * inv;
+        const float o2 = oacc[db][4 * r4 + 2] * inv, o3 = oacc[db][4 * r4 + 3] * inv;
+        if constexpr (OUT_BF16) {
+          u32x2 w;
+          w[0] = pack_bf16(o0, o1);
+          w[1] = pack_bf16(o2, o3);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o) + orow + d0) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
+        }
+      }
+    if (lse && hl == 0)
+      lse[((int64_t)b * Hq + h) * S + row] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
+  }
+}
+
+template <int D, bool CAUSAL, bool ROPE, bool OUT_BF16>
+hipError_t go(const PrefillArgs& a, hipStream_t st) {
+  const int G = a.Hq / a.Hkv;
+  const int nqb = (a.S + kBM - 1) / kBM;
+  const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
+  const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, ROPE, OUT_BF16>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+                     (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.pos0,
+                     reinterpret_cast<const float2*>(a.table));
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t dispatch_d(const PrefillArgs& a, hipStream_t st) {
+  const bool rope = a.table != nullptr;
+  if (a.causal) {
+    if (rope) return a.out_bf16 ? go<D, true, true, true>(a, st) : go<D, true, true, false>(a, st);
+    return a.out_bf16 ? go<D, true, false, true>(a, st) : go<D, true, false, false>(a, st);
+  }
+  if (rope) return a.out_bf16 ? go<D, false, true, true>(a, st) : go<D, false, true, false>(a, st);
+  return a.out_bf16 ? go<D, false, false, true>(a, st) : go<D, false, false, false>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
+  return a.D == 64 ? dispatch_d<64>(a, st) : dispatch_d<128>(a, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,135 @@
+// Rotary position embeddings: coefficient table and the stand-alone rotation kernel.
+//
+// The rotation follows "Transformer Architecture & Self-Attention Mechanics" (devthesis.com),
+// section 3, "Rotary Position Embeddings (RoPE)": adjacent pairs (x[2i], x[2i+1]) of a head
+// vector at position m are turned counter-clockwise by m * theta_i, theta_i = base^(-2i/D).
+// The frequencies match the NumPy example of "Transformer Architecture: FlashAttention & RoPE"
+// (academy.kwas.tech).
+//
+// rope_apply is HBM-bound: it reads and writes every element once (plus the table row, which
+// stays in L2 across heads).  Each lane moves 16 bytes of x for bf16 (4 pairs) or fp32
+// (2 pairs), so loads and stores are dwordx4 and coalesced along D.
+#include "common.h"
+
+namespace attn {
+
+// table[m][i] = (cos(m * theta_i), sin(m * theta_i)); angle formed in double precision.
+__global__ void rope_table_kernel(float2* __restrict__ table, int max_pos, int half, double base) {
+  const int64_t n = (int64_t)max_pos * half;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int m = (int)(idx / half);
+    const int i = (int)(idx - (int64_t)m * half);
+    const double theta = pow(base, -2.0 * (double)i / (double)(2 * half));
+    const double ang = (double)m * theta;
+    table[idx] = make_float2((float)cos(ang), (float)sin(ang));
+  }
+}
+
+hipError_t launch_rope_table(float* table, int max_pos, int D, double base, hipStream_t st) {
+  const int half = D / 2;
+  const int64_t n = (int64_t)max_pos * half;
+  const int threads = 256;
+  int64_t blocks = (n + threads - 1) / threads;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
+                     reinterpret_cast<float2*>(table), max_pos, half, base);
+  return hipGetLastError();
+}
+
+// PPT pairs per lane.  Rows are [rows_total = B*H*S][D]; row r sits at position pos0 + r % S.
+template <bool BF16, int PPT>
+__global__ void rope_apply_kernel(const void* x, void* out, int64_t rows,
+                                  int S, int D, int pos0, const float2* __restrict__ table) {
+  const int half = D / 2;
+  const int lanes_per_row = half / PPT;
+  const int64_t n = rows * lanes_per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = idx / lanes_per_row;
+    const int p0 = (int)(idx - row * lanes_per_row) * PPT;  // first pair of this lane
+    const int pos = pos0 + (int)(row % S);
+    const float2* tr = table + (int64_t)pos * half + p0;
+    float v[2 * PPT];
+    if constexpr (BF16) {
+      const uint16_t* src = reinterpret_cast<const uint16_t*>(x) + row * D + 2 * p0;
+      if constexpr (PPT == 4) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) { v[2 * j] = bf16lo(w[j]); v[2 * j + 1] = bf16hi(w[j]); }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2 * PPT; ++j) v[j] = __uint_as_float((uint32_t)src[j] << 16);
+      }
+    } else {
+      const float* src = reinterpret_cast<const float*>(x) + row * D + 2 * p0;
+      if constexpr (PPT == 2) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = w[j];
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2 * PPT; ++j) v[j] = src[j];
+      }
+    }
+    float r[2 * PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+      const float2 cs = tr[j];
+      r[2 * j] = v[2 * j] * cs.x - v[2 * j + 1] * cs.y;
+      r[2 * j + 1] = v[2 * j] * cs.y + v[2 * j + 1] * cs.x;
+    }
+    if constexpr (BF16) {
+      uint16_t* dst = reinterpret_cast<uint16_t*>(out) + row * D + 2 * p0;
+      if constexpr (PPT == 4) {
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = pack_bf16(r[2 * j], r[2 * j + 1]);
+        *reinterpret_cast<u32x4*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < PPT; ++j) {
+          const uint32_t w = pack_bf16(r[2 * j], r[2 * j + 1]);
+          dst[2 * j] = (uint16_t)(w & 0xffffu);
+          dst[2 * j + 1] = (uint16_t)(w >> 16);
+        }
+      }
+    } else {
+      float* dst = reinterpret_cast<float*>(out) + row * D + 2 * p0;
+      if constexpr (PPT == 2) {
+        f32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = r[j];
+        *reinterpret_cast<f32x4*>(dst) = w;
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2 * PPT; ++j) dst[j] = r[j];
+      }
+    }
+  }
+}
+
+template <bool BF16, int PPT>
+static hipError_t rope_apply_go(const void* x, void* out, int64_t rows, int S, int D, int pos0,
+                                const float* table, hipStream_t st) {
+  const int64_t n = rows * (D / 2 / PPT);
+  const int threads = 256;
+  int64_t blocks = (n + threads - 1) / threads;
+  if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 blocks per CU
+  hipLaunchKernelGGL((rope_apply_kernel<BF16, PPT>), dim3((unsigned)blocks), dim3(threads), 0, st,
+                     x, out, rows, S, D, pos0, reinterpret_cast<const float2*>(table));
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_apply(const void* x, void* out, bool bf16, int64_t rows, int S, int D,
+                             int pos0, const float* table, hipStream_t st) {
+  const int half = D / 2;
+  if (bf16) {
+    if (half % 4 == 0) return rope_apply_go<true, 4>(x, out, rows, S, D, pos0, table, st);
+    return rope_apply_go<true, 1>(x, out, rows, S, D, pos0, table, st);
+  }
+  if (half % 2 == 0) return rope_apply_go<false, 2>(x, out, rows, S, D, pos0, table, st);
+  return rope_apply_go<false, 1>(x, out, rows, S, D, pos0, table, st);
+}
+
+}  // namespace attn

@@ -1,0 +1,220 @@
+"""Thin ctypes binding of libattn.so (the C ABI declared in include/attn.h).
+
+Argument marshalling only: each function takes torch tensors that already live on the GPU,
+checks the things ctypes cannot (dtype, contiguity, device), and passes raw pointers, sizes
+and the current HIP stream to the same-named C entry point.  Every step of the computation
+runs in the library's HIP kernels; there is no fallback path.  Importing this module raises
+if the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads torch's HIP runtime first, so libattn.so binds to the same one
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+
+ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
+ATTN_F32, ATTN_BF16 = 0, 1
+
+EXPORTED = (
+    "attn_version",
+    "attn_status_string",
+    "attn_rope_table_bytes",
+    "attn_rope_table_init",
+    "attn_rope_apply",
+    "attn_prefill",
+    "attn_decode_workspace_bytes",
+    "attn_decode_num_splits",
+    "attn_decode",
+)
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)}")
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m transformer_self_attention_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
+    lib.attn_version.restype = i32
+    lib.attn_version.argtypes = []
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [i32]
+    lib.attn_rope_table_bytes.restype = sz
+    lib.attn_rope_table_bytes.argtypes = [i32, i32]
+    lib.attn_rope_table_init.restype = i32
+    lib.attn_rope_table_init.argtypes = [fp, i32, i32, ctypes.c_double, vp]
+    lib.attn_rope_apply.restype = i32
+    lib.attn_rope_apply.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, fp, i32, vp]
+    lib.attn_prefill.restype = i32
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                 fp, i32, vp]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.attn_decode_num_splits.restype = i32
+    lib.attn_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
+    lib.attn_decode.restype = i32
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, fp,
+                                i32, i32, vp, sz, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw():
+    """The ctypes handle itself (for tests of the C ABI)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.attn_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return int(_lib.attn_version())
+
+
+def _check(status: int, where: str):
+    if status != ATTN_OK:
+        raise AttnError(status, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return ATTN_BF16
+    if t.dtype == torch.float32:
+        return ATTN_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def rope_table_bytes(max_pos: int, D: int) -> int:
+    return int(_lib.attn_rope_table_bytes(max_pos, D))
+
+
+def rope_table_init(table: torch.Tensor, max_pos: int, D: int, base: float = 10000.0, stream=None):
+    """Fill float32 table [max_pos, D/2, 2] with (cos, sin) of m * base^(-2i/D)."""
+    _need(table, "table")
+    if table.dtype != torch.float32 or table.numel() * 4 < rope_table_bytes(max_pos, D):
+        raise ValueError("table must be float32 with at least rope_table_bytes() bytes")
+    _check(_lib.attn_rope_table_init(_ptr(table), max_pos, D, float(base), _stream(stream)),
+           "attn_rope_table_init")
+
+
+def make_rope_table(max_pos: int, D: int, base: float = 10000.0, device="cuda", stream=None) -> torch.Tensor:
+    t = torch.empty((max_pos, D // 2, 2), dtype=torch.float32, device=device)
+    rope_table_init(t, max_pos, D, base, stream)
+    return t
+
+
+def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.Tensor = None, stream=None):
+    """Rotate x [B, H, S, D] at positions pos0 + s (out=None: new tensor; out=x: in place)."""
+    _need(x, "x")
+    _need(table, "table")
+    B, H, S, D = x.shape
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out")
+    if out.shape != x.shape or out.dtype != x.dtype:
+        raise ValueError("out must match x")
+    _check(_lib.attn_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, S, D, pos0, _ptr(table),
+                                table.shape[0], _stream(stream)), "attn_rope_apply")
+    return out
+
+
+def prefill(q, k, v, table=None, *, causal=True, pos0=0, out=None, out_dtype=None, lse=None,
+            stream=None):
+    """o = softmax(rope(q) rope(k)^T / sqrt(D)) v over [B, H, S, D] tensors (GQA when Hkv < Hq)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
+        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise ValueError("q, k, v must share a dtype")
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    if lse is not None:
+        _need(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != B * Hq * S:
+            raise ValueError("lse must be float32 [B, Hq, S]")
+    tmax = 0
+    if table is not None:
+        _need(table, "table")
+        tmax = table.shape[0]
+    _check(_lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq,
+                             Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), tmax, _stream(stream)),
+           "attn_prefill")
+    return out
+
+
+def decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split=0) -> int:
+    return int(_lib.attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split))
+
+
+def decode_num_splits(B, Hq, Hkv, S_max, D, n_split=0) -> int:
+    return int(_lib.attn_decode_num_splits(B, Hq, Hkv, S_max, D, n_split))
+
+
+def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, out=None, out_dtype=None,
+           lse=None, workspace=None, stream=None):
+    """One query per sequence (q [B, Hq, 1, D]) against the cache [B, Hkv, S_max, D]."""
+    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len")):
+        _need(t, n)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, Hq, 1, D]")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B:
+        raise ValueError("cache_len must be int32 [B]")
+    if q_pos is not None:
+        _need(q_pos, "q_pos")
+        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
+            raise ValueError("q_pos must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    need = decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    tmax = 0
+    if table is not None:
+        _need(table, "table")
+        tmax = table.shape[0]
+    _check(_lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(q_pos),
+                            _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _ptr(table), tmax,
+                            n_split, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                            _stream(stream)), "attn_decode")
+    return out
