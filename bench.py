@@ -65,20 +65,31 @@ def time_launches(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps   # ms per call
 
 
-def bench_prefill(lib, inputs, wl, steps, warmup):
+def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
+    """Times one prefill step (keys rotated once into a workspace + the attention kernel), and
+    separately the attention kernel alone, the key-rotation pass alone and the fused variant."""
     import torch
     log(f"[bench] generating {wl.name} prefill inputs B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} S={wl.S} D={wl.D}")
     p = inputs.make_prefill(wl)
     q, k, v = p.q.torch("cuda"), p.k.torch("cuda"), p.v.torch("cuda")
     tab = lib.make_rope_table(wl.S, wl.D)
     out = torch.empty_like(q)
+    ws = torch.empty(lib.prefill_workspace_bytes(wl.B, wl.Hkv, wl.S, wl.D), dtype=torch.uint8, device="cuda")
+    krot = ws.view(torch.float16).view(k.shape)
     torch.cuda.synchronize()
-    log(f"[bench] timing {wl.name} prefill: warmup {warmup}, steps {steps}")
-    ms = time_launches(lambda: lib.prefill(q, k, v, tab, out=out), steps, warmup)
     flops = wl.prefill_flops()
-    tflops = flops / (ms * 1e-3) / 1e12
-    log(f"[bench] {wl.name} prefill: {ms:.4f} ms/launch, {tflops:.1f} TFLOP/s")
-    return p, ms, tflops
+    log(f"[bench] timing {wl.name} prefill step: warmup {warmup}, steps {steps}")
+    r = {"p": p}
+    r["ms_step"] = time_launches(lambda: lib.prefill(q, k, v, tab, out=out, workspace=ws), steps, warmup)
+    if variants:
+        r["ms_kernel"] = time_launches(lambda: lib.prefill_prerotated(q, krot, v, tab, out=out), steps, warmup)
+        r["ms_rope"] = time_launches(lambda: lib.rotate_keys_f16(k, tab, out=krot), steps, warmup)
+        r["ms_fused"] = time_launches(lambda: lib.prefill(q, k, v, tab, out=out), steps, warmup)
+    for key in ("ms_step", "ms_kernel", "ms_fused"):
+        if key in r:
+            r[key.replace("ms_", "tflops_")] = flops / (r[key] * 1e-3) / 1e12
+    log(f"[bench] {wl.name} prefill: " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in r.items() if k_ != "p"))
+    return r
 
 
 def bench_decode(lib, inputs, wl, steps, warmup):
@@ -173,7 +184,8 @@ def main():
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], args.steps, args.warmup)
     if args.long or args.only == "long":
-        res["long"] = bench_prefill(lib, inputs, W["long"], max(2, args.steps // 4), min(args.warmup, 2))
+        res["long"] = bench_prefill(lib, inputs, W["long"], max(2, args.steps // 4), min(args.warmup, 2),
+                                    variants=False)
 
     out = {
         "metric": "causal GQA prefill TFLOP/s (% MFMA peak); decode KV-read GB/s (% HBM peak)",
@@ -182,18 +194,24 @@ def main():
         "dtype": "bf16", "data": "synthetic",
     }
     if "prefill" in res:
-        p, ms, tflops = res["prefill"]
+        r = res["prefill"]
+        p, ms, tflops = r["p"], r["ms_step"], r["tflops_step"]
+        kern_tflops = r.get("tflops_kernel", tflops)
         wl = p.wl
         out.update({
             "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
+            "step_parts": {"rotate_keys_f16_ms": round(r.get("ms_rope", float("nan")), 5),
+                           "attention_kernel_ms": round(r.get("ms_kernel", float("nan")), 5),
+                           "fused_rope_variant_ms": round(r.get("ms_fused", float("nan")), 5),
+                           "fused_rope_variant_tflops": round(r.get("tflops_fused", float("nan")), 2)},
             "operand_dtypes": {"inputs": "bf16", "qk_mfma": "f16", "pv_mfma": "bf16", "accumulate": "f32",
                                "output": "bf16"},
             "config": {"workload": "GQA causal prefill with fused RoPE", "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
                        "seq_len": wl.S, "head_dim": wl.D, "causal": True, "rope_base": wl.rope_base,
                        "flops_per_step": wl.prefill_flops()},
-            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel", "achieved": round(tflops, 2),
-                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated keys)",
+                         "achieved": round(kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                          "traffic": MEASURED_TRAFFIC["prefill_gqa"]},
         })
     if "decode" in res:
@@ -210,7 +228,8 @@ def main():
                         "config": dec["config"], "roofline": dec["roofline"]})
         out["decode"] = dec
     if "long" in res:
-        p, ms, tflops = res["long"]
+        r = res["long"]
+        p, ms, tflops = r["p"], r["ms_step"], r["tflops_step"]
         out["long_prefill"] = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
                                "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
                                "config": {"B": p.wl.B, "Hq": p.wl.Hq, "Hkv": p.wl.Hkv, "seq_len": p.wl.S,
@@ -218,7 +237,7 @@ def main():
     if not args.no_cpu_baseline:
         if "prefill" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, prefill sample)")
-            out["cpu_baseline"] = cpu_baseline_prefill(res["prefill"][0])
+            out["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["p"])
         if "decode" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, decode sample)")
             cb = cpu_baseline_decode(res["decode"][0])

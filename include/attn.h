@@ -103,19 +103,45 @@ attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int 
  * causal != 0 masks key j > query i (square mask anchored at the top-left); causal == 0
  *      lets every query see every key.
  * Scale: 1/sqrt(D), fixed.
+ * workspace: optional device scratch of at least attn_prefill_workspace_bytes(B, Hkv, S, D)
+ *      bytes (contents on entry irrelevant, overwritten).  Used only for bf16 input with RoPE:
+ *      the keys are then rotated once, in one pass, into the workspace, and the attention
+ *      kernel streams the rotated keys.  With workspace == NULL the key rotation is fused into
+ *      every K tile load instead (same results; more arithmetic per tile).
  *
  * Support matrix: D in {64, 128}; in_dt = ATTN_F32 (float32 arithmetic throughout, out_dt
- * must be ATTN_F32) or in_dt = ATTN_BF16 (out_dt either).  For bf16 input the rotated
- * q and k are rounded to IEEE half precision for the Q.K^T matrix-core product (fp32
- * accumulation), so |q|, |k| must stay below 4.6e4; the softmax weights are rounded to
- * bf16 for the P.V product (fp32 accumulation).
+ * must be ATTN_F32) or in_dt = ATTN_BF16 (out_dt either).  For bf16 input with RoPE the
+ * rotated q and k are rounded to IEEE half precision for the Q.K^T matrix-core product
+ * (fp32 accumulation), so |q|, |k| must stay below 4.6e4; without RoPE the bf16 inputs are
+ * multiplied exactly.  The softmax weights are rounded to bf16 for the P.V product (fp32
+ * accumulation).
  * Errors: ATTN_ERR_INVALID_ARG for null q/k/v/o, B/Hq/Hkv/S < 1, Hq % Hkv != 0, bad RoPE
- * range, misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * range, a workspace that is misaligned or too small, misalignment; ATTN_ERR_UNSUPPORTED
+ * outside the support matrix.
  * --------------------------------------------------------------------------------------- */
+size_t attn_prefill_workspace_bytes(int B, int Hkv, int S, int D);
 attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                          attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
                          int causal, int pos0, const float* rope_table, int table_max_pos,
-                         void* stream);
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * The two stages of attn_prefill with a workspace, callable on their own (for example to
+ * rotate a sequence's keys once and run several query batches against them).
+ *
+ * attn_rotate_keys_f16: k_rot[b,h,s,:] = RoPE(k[b,h,s,:]) at position pos0 + s, computed in
+ *   float32 from bf16 k [B, Hkv, S, D] and stored as IEEE half precision (same layout).
+ * attn_prefill_prerotated: attn_prefill for bf16 q and v with RoPE, whose keys were already
+ *   rotated by attn_rotate_keys_f16 with the same table and pos0 (k_rot is read as fp16 and
+ *   never rotated again; q is rotated at pos0 + s).  Other arguments as in attn_prefill.
+ * Support matrix: D in {64, 128}.  Errors as in attn_prefill (rope_table is required).
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
+                                 const float* rope_table, int table_max_pos, void* stream);
+attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void* v, void* o,
+                                    float* lse, attn_dtype out_dt, int B, int Hq, int Hkv, int S,
+                                    int D, int causal, int pos0, const float* rope_table,
+                                    int table_max_pos, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV

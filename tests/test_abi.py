@@ -51,11 +51,11 @@ def test_rope_table_bytes():
 
 def _prefill(**kw):
     a = dict(q=A, k=A, v=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=1, Hq=8, Hkv=2, S=100, D=128,
-             causal=1, pos0=0, table=A, tmax=100, stream=None)
+             causal=1, pos0=0, table=A, tmax=100, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.raw().attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["in_dt"], a["out_dt"], a["B"],
                                   a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["pos0"], a["table"],
-                                  a["tmax"], a["stream"])
+                                  a["tmax"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -66,6 +66,7 @@ def _prefill(**kw):
     (dict(D=65), INV), (dict(in_dt=7), INV), (dict(out_dt=-1), INV),
     (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP), (dict(in_dt=F32, out_dt=BF16), UNSUP),
     (dict(D=96, table=None), UNSUP),
+    (dict(ws=A, wsb=2 * 100 * 128 * 2 - 1), INV), (dict(ws=MIS, wsb=1 << 20), INV),
 ])
 def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
@@ -109,6 +110,26 @@ def test_rope_apply_rejects():
     assert call(dt=3) == INV
 
 
+def test_two_stage_prefill_rejects():
+    raw = lib.raw()
+    rot = lambda k=A, out=A, B=1, H=2, S=10, D=128, pos0=0, table=A, tmax=10: raw.attn_rotate_keys_f16(
+        k, out, B, H, S, D, pos0, table, tmax, None)
+    assert rot(k=None) == INV
+    assert rot(table=None) == INV
+    assert rot(pos0=1) == INV
+    assert rot(out=MIS) == INV
+    assert rot(D=96) == UNSUP
+    pre = lambda q=A, k=A, v=A, o=A, lse=None, odt=BF16, B=1, Hq=4, Hkv=2, S=10, D=128, causal=1, pos0=0, \
+        table=A, tmax=10: raw.attn_prefill_prerotated(q, k, v, o, lse, odt, B, Hq, Hkv, S, D, causal, pos0,
+                                                      table, tmax, None)
+    assert pre(table=None) == INV
+    assert pre(Hkv=3) == INV
+    assert pre(k=MIS) == INV
+    assert pre(odt=5) == INV
+    assert pre(tmax=9) == INV
+    assert pre(D=64 + 32) == UNSUP
+
+
 def test_rope_table_init_rejects():
     raw = lib.raw()
     assert raw.attn_rope_table_init(None, 10, 8, 10000.0, None) == INV
@@ -117,6 +138,11 @@ def test_rope_table_init_rejects():
     assert raw.attn_rope_table_init(A, 10, 8, 1.0, None) == INV
     assert raw.attn_rope_table_init(A, 10, 8, float("nan"), None) == INV
     assert raw.attn_rope_table_init(MIS, 10, 8, 10000.0, None) == INV
+
+
+def test_prefill_workspace_bytes():
+    assert lib.prefill_workspace_bytes(1, 8, 8192, 128) == 8 * 8192 * 128 * 2
+    assert lib.prefill_workspace_bytes(0, 8, 8192, 128) == 0
 
 
 def test_decode_workspace_geometry():

@@ -85,12 +85,16 @@ def test_rope_apply_random(lib, dtype, D, S, pos0, inplace):
 # ------------------------------------------------------------------------------------------
 # Prefill
 # ------------------------------------------------------------------------------------------
-def run_prefill(lib, p, *, causal=True, out_dtype=None, rope=True, pos0=0):
+def run_prefill(lib, p, *, causal=True, out_dtype=None, rope=True, pos0=0, workspace=True):
+    """workspace=True: keys rotated once into a workspace; False: rotation fused per K tile."""
     wl = p.wl
     tab = lib.make_rope_table(pos0 + wl.S, wl.D) if rope else None
     q, k, v = dev(p.q), dev(p.k), dev(p.v)
     lse = torch.empty((wl.B, wl.Hq, wl.S), dtype=torch.float32, device="cuda")
-    o = lib.prefill(q, k, v, tab, causal=causal, pos0=pos0, out_dtype=out_dtype, lse=lse)
+    ws = None
+    if workspace:
+        ws = torch.empty(lib.prefill_workspace_bytes(wl.B, wl.Hkv, wl.S, wl.D), dtype=torch.uint8, device="cuda")
+    o = lib.prefill(q, k, v, tab, causal=causal, pos0=pos0, out_dtype=out_dtype, lse=lse, workspace=ws)
     torch.cuda.synchronize()
     return o, lse
 
@@ -133,12 +137,15 @@ def test_prefill_fp32_ragged(lib, B, Hq, Hkv, S, D, causal):
     (1, 8, 8, 64, 128, True, "f32"), (2, 2, 2, 1, 128, True, "bf16"), (1, 16, 4, 515, 128, True, "f32"),
     (1, 4, 2, 250, 64, False, "f32"),
 ])
-def test_prefill_bf16_ragged(lib, B, Hq, Hkv, S, D, causal, out):
-    banner(f"prefill bf16 B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} out={out}")
+@pytest.mark.parametrize("mode", ["workspace", "fused", "norope"])
+def test_prefill_bf16_ragged(lib, B, Hq, Hkv, S, D, causal, out, mode):
+    banner(f"prefill bf16 B={B} Hq={Hq} Hkv={Hkv} S={S} D={D} causal={causal} out={out} mode={mode}")
     wl = inputs.Workload("t", B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype="bf16", seed=7 * S + D, kind="prefill")
     p = inputs.make_prefill(wl)
-    o, lse = run_prefill(lib, p, causal=causal, out_dtype=torch.float32 if out == "f32" else torch.bfloat16)
-    ref, ref_lse = oracle_rows(p, causal=causal)
+    rope = mode != "norope"
+    o, lse = run_prefill(lib, p, causal=causal, out_dtype=torch.float32 if out == "f32" else torch.bfloat16,
+                         rope=rope, workspace=mode == "workspace")
+    ref, ref_lse = oracle_rows(p, causal=causal, rope=rope)
     assert_bf16_parity(to_np(o), ref, "o")
     mx, _ = err_stats(to_np(lse), ref_lse)
     assert mx < 2e-2
@@ -156,14 +163,16 @@ def test_prefill_mha_config(lib):
 
 
 def test_prefill_gqa_config(lib):
-    """GQA workload at full size: B=1, Hq=64, Hkv=8, S=8192, D=128; 256 seeded rows per head."""
+    """GQA workload at full size: B=1, Hq=64, Hkv=8, S=8192, D=128; 256 seeded rows per head.
+    Both key paths: rotated once into a workspace (the benchmarked path) and fused per tile."""
     wl = inputs.WORKLOADS["gqa"]
     banner("prefill GQA Hq=64 Hkv=8 S=8192 (full config, 256 rows/head)")
     p = inputs.make_prefill(wl)
-    o, lse = run_prefill(lib, p)
     ref, ref_lse = oracle_rows(p, rows=p.rows)
-    assert_bf16_parity(take_rows(to_np(o), p.rows), ref, "gqa o")
-    assert err_stats(take_rows(to_np(lse), p.rows), ref_lse)[0] < 2e-2
+    for ws in (True, False):
+        o, lse = run_prefill(lib, p, workspace=ws)
+        assert_bf16_parity(take_rows(to_np(o), p.rows), ref, f"gqa o (workspace={ws})")
+        assert err_stats(take_rows(to_np(lse), p.rows), ref_lse)[0] < 2e-2
 
 
 def test_prefill_long_config(lib):
@@ -175,13 +184,33 @@ def test_prefill_long_config(lib):
     banner("prefill long Hq=32 Hkv=8 S=32768 x8 keys (full config, 128 rows/head)")
     p = inputs.make_prefill(wl)
     ref, ref_lse = oracle_rows(p, rows=p.rows)
-    o, lse = run_prefill(lib, p, out_dtype=torch.float32)
-    assert_bf16_parity(take_rows(to_np(o), p.rows), ref, "long o (fp32 out)")
-    assert err_stats(take_rows(to_np(lse), p.rows), ref_lse)[0] < 2e-2
+    for ws in (True, False):
+        o, lse = run_prefill(lib, p, out_dtype=torch.float32, workspace=ws)
+        assert_bf16_parity(take_rows(to_np(o), p.rows), ref, f"long o (fp32 out, workspace={ws})")
+        assert err_stats(take_rows(to_np(lse), p.rows), ref_lse)[0] < 2e-2
     ob, _ = run_prefill(lib, p, out_dtype=torch.bfloat16)
     mx, mean = err_stats(take_rows(to_np(ob), p.rows), ref)
     print(f"    long o (bf16 out) max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
     assert mx <= 2e-2
+
+
+def test_two_stage_prefill_equals_one_call(lib):
+    """rotate_keys_f16 + prefill_prerotated is exactly prefill with a workspace; the rotated
+    keys match the oracle's rotation to fp16 rounding."""
+    banner("two-stage prefill == one call; rotated keys vs oracle")
+    wl = inputs.Workload("t", B=2, Hq=8, Hkv=2, S=300, D=128, dtype="bf16", seed=41, kind="prefill")
+    p = inputs.make_prefill(wl)
+    tab = lib.make_rope_table(310, 128)
+    q, k, v = dev(p.q), dev(p.k), dev(p.v)
+    krot = lib.rotate_keys_f16(k, tab, pos0=7)
+    o2 = lib.prefill_prerotated(q, krot, v, tab, pos0=7)
+    ws = torch.empty(lib.prefill_workspace_bytes(2, 2, 300, 128), dtype=torch.uint8, device="cuda")
+    o1 = lib.prefill(q, k, v, tab, pos0=7, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ref_k = oracle.rope(p.k.f64(), 7 + np.arange(300))
+    got_k = to_np(krot)
+    assert np.all(np.abs(got_k - ref_k) <= np.abs(ref_k) * 2.0 ** -10 + 1e-6)   # one fp16 rounding
 
 
 # ------------------------------------------------------------------------------------------

@@ -88,10 +88,15 @@ attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int 
                                           (hipStream_t)stream));
 }
 
+size_t attn_prefill_workspace_bytes(int B, int Hkv, int S, int D) {
+  if (B < 1 || Hkv < 1 || S < 1 || D < 1) return 0;
+  return attn::prefill_workspace_bytes(B, Hkv, S, D);
+}
+
 attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                          attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
                          int causal, int pos0, const float* rope_table, int table_max_pos,
-                         void* stream) {
+                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return ATTN_ERR_INVALID_ARG;
@@ -100,6 +105,9 @@ attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, f
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_INVALID_ARG;
   if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (workspace && (!aligned16(workspace) ||
+                    workspace_bytes < attn::prefill_workspace_bytes(B, Hkv, S, D)))
+    return ATTN_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
   if (in_dt == ATTN_F32 && out_dt != ATTN_F32) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)B * Hq * S > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
@@ -111,8 +119,42 @@ attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, f
   a.causal = causal != 0;
   a.pos0 = pos0;
   a.table = rope_table;
+  a.workspace = (rope_table && in_dt == ATTN_BF16) ? workspace : nullptr;
   hipStream_t st = (hipStream_t)stream;
   return from_hip(in_dt == ATTN_F32 ? attn::launch_prefill_f32(a, st) : attn::launch_prefill_bf16(a, st));
+}
+
+attn_status attn_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
+                                 const float* rope_table, int table_max_pos, void* stream) {
+  if (!k || !k_rot || !rope_table) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || S < 1 || D < 1 || (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(k_rot)) return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  return from_hip(attn::launch_rotate_keys_f16(k, k_rot, B, Hkv, S, D, pos0, rope_table, (hipStream_t)stream));
+}
+
+attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void* v, void* o, float* lse,
+                                    attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D, int causal,
+                                    int pos0, const float* rope_table, int table_max_pos, void* stream) {
+  if (!q || !k_rot || !v || !o || !rope_table) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_rot) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
+    return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * S > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  attn::PrefillArgs a;
+  a.q = q; a.k = k_rot; a.v = v; a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+  a.causal = causal != 0;
+  a.pos0 = pos0;
+  a.table = rope_table;
+  a.workspace = nullptr;
+  return from_hip(attn::launch_prefill_prerotated(a, k_rot, (hipStream_t)stream));
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {

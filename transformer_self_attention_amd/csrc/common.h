@@ -69,10 +69,15 @@ struct PrefillArgs {
   bool causal;
   int pos0;
   const float* table;  // nullptr: no RoPE
+  void* workspace;     // bf16 path: room for the rotated fp16 keys, or nullptr (RoPE fused)
 };
 
+size_t prefill_workspace_bytes(int B, int Hkv, int S, int D);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
+hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
+                                  const float* table, hipStream_t st);
+hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st);
 
 struct DecodeArgs {
   const void* q;

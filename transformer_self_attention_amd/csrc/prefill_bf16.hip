@@ -1,30 +1,37 @@
 // bf16 prefill on the gfx950 matrix cores: exact attention tiled with an online softmax.
 //
 // Method: scaled dot-product attention, devthesis.com "Transformer Architecture & Self-Attention
-// Mechanics" section 1; causal mask of the learnllm.online listing; RoPE of devthesis section 3
-// fused into the Q and K tile loads; the tiling with a running row max and row sum of
-// codingpancake.com "Building Self-Attention and Transformer Engines" sections 4.1-4.2 (the score
-// tile never leaves registers); GQA head sharing of the same page, section 6.1.
+// Mechanics" section 1; causal mask of the learnllm.online listing; RoPE of devthesis section 3;
+// the tiling with a running row max and row sum of codingpancake.com "Building Self-Attention and
+// Transformer Engines" sections 4.1-4.2 (the score tile never leaves registers); GQA head sharing
+// of the same page, section 6.1.
 //
-// Shape of the kernel (one workgroup = 4 waves = 128 query rows of one head):
-//  * Each wave owns 32 query rows.  Its rotated Q (scaled by log2(e)/sqrt(D), fp16) sits in
-//    registers as the B operand of v_mfma_f32_32x32x16_f16.
-//  * Keys arrive in tiles of 64, double-buffered in LDS: K rotated in fp32 and stored as fp16,
-//    V stored as bf16, both with an XOR swizzle of 16-byte chunks so that the MFMA operand reads
-//    are bank-conflict free.
-//  * Scores are computed transposed, S^T = K Q^T, so that each lane holds 32 scores of ONE
-//    query row (the other 32 of the tile sit in lane l^32): the row max is a local max3 tree
-//    plus one v_permlane32_swap; the row sum stays lane-local until the end.
-//  * P (bf16) is consumed straight from those registers as the B operand of the P.V product
-//    O^T += V^T P^T; the V^T operand comes from LDS through ds_read_b64_tr_b16.  The key order
-//    inside the contraction is permuted so that no register shuffle is needed.
-//  * Online softmax in log2 units with lazy rescaling: O and l are rescaled only when a row's
-//    max grows by more than 8 (so unnormalised weights stay <= 2^8); the result is the same
-//    softmax, normalised once at the end.
-//  * Causal: tiles entirely above a wave's rows are skipped; only tiles crossing the diagonal
-//    (or the tail S) are masked.
-//  * Workgroup order: heaviest query blocks first; the G query heads sharing one KV head (and
-//    the same query block) are sent to the same XCD so its L2 serves their K/V reads.
+// Shape of the kernel (one workgroup = 4 waves = 128 query rows of one head, two workgroups per
+// CU):
+//  * Each wave owns 32 query rows.  Its Q rows sit in registers as the B operand of a 32x32x16
+//    MFMA: rotated in fp32, scaled by log2(e)/sqrt(D) and rounded to fp16 when RoPE is on; raw
+//    bf16 (exact) when it is off.
+//  * Keys arrive in tiles of 64, double-buffered in LDS with an XOR swizzle of 16-byte chunks
+//    (bank-conflict-free operand reads).  Three ways to fill the K tile:
+//      KMODE_PREROT  keys already rotated to fp16 by a one-pass kernel (workspace given): K and V
+//                    tiles go HBM -> LDS with global_load_lds_dwordx4, no register staging;
+//      KMODE_FUSED   RoPE fused into the K tile load: bf16 K and the coefficient rows are staged
+//                    in registers, rotated in fp32, stored to LDS as fp16;
+//      KMODE_RAW     no RoPE: bf16 K straight to LDS; Q.K^T on bf16 operands (exact products),
+//                    the scale folded into the exponent.
+//    V always goes HBM -> LDS directly.
+//  * Scores are computed transposed, S^T = K Q^T, so that each lane holds 32 scores of ONE query
+//    row (the other 32 of the tile sit in lane l^32): the row max is a local max3 tree plus one
+//    v_permlane32_swap; the row sum stays lane-local until the end.
+//  * P (bf16) is consumed straight from those registers as the B operand of O^T += V^T P^T; the
+//    V^T operand comes from LDS through ds_read_b64_tr_b16.  The key order inside the contraction
+//    is permuted so that no register shuffle is needed.
+//  * Online softmax in log2 units with lazy rescaling: O and l are rescaled only when a row's max
+//    grows by more than 8 (unnormalised weights stay <= 2^8); normalised once at the end.
+//  * Causal: tiles entirely above a wave's rows are skipped; only tiles crossing the diagonal (or
+//    the tail S) are masked.
+//  * Workgroup order: heaviest query blocks first; the G query heads sharing one KV head (and the
+//    same query block) go to the same XCD so its L2 serves their K/V reads.
 #include "common.h"
 
 namespace attn {
@@ -38,8 +45,11 @@ constexpr int kBM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
 constexpr int kBN = 64;                     // keys per tile
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kNumXcd = 8;
+constexpr int kWaitVmcnt0 = 0x0F70;          // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 
-// Physical 16-byte chunk of logical chunk `lc` in LDS row `r`.
+enum { KMODE_PREROT = 0, KMODE_FUSED = 1, KMODE_RAW = 2 };
+
+// Physical 16-byte chunk of logical chunk `lc` in LDS row `r` (an involution in lc).
 template <int D>
 __device__ __forceinline__ int swz(int r, int lc) {
   if constexpr (D == 128) {
@@ -49,7 +59,7 @@ __device__ __forceinline__ int swz(int r, int lc) {
   }
 }
 
-template <int D, bool CAUSAL, bool ROPE, bool OUT_BF16>
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
 __global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
@@ -58,8 +68,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over D
   constexpr int DB = D / 32;                 // 32-wide output blocks over D
-  constexpr int CPT = kBN * NCH / kThreads;  // chunks of K (and of V) per thread per tile
   constexpr int TILE_ELEMS = kBN * D;
+  constexpr int DIRECT_PER_WAVE = TILE_ELEMS * 2 / 1024 / kWaves;  // 1 KB wave-loads per tensor
+  constexpr int CPT = kBN * NCH / kThreads;  // K chunks per thread (fused mode)
+  constexpr bool QK_BF16 = KMODE == KMODE_RAW;
 
   __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TILE_ELEMS];
@@ -85,13 +97,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int wave = tid >> 6;
   const int hl = lane >> 5;      // which half of the wave
   const int l32 = lane & 31;
+  const int g16 = lane >> 4;     // 16-lane group
+  const int i16 = lane & 15;
   const int q0 = qblock * kBM;
   const int qw = q0 + wave * kRowsPerWave;  // first row of this wave
   const int row = qw + l32;                 // this lane's query row
-  const float qscale = 1.4426950408889634f / sqrtf((float)D);
+  // exp2 argument scale: folded into Q (fp16 modes) or applied to raw scores (bf16 mode)
+  const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
 
-  // ---- Q: load, rotate, scale, convert to fp16 B-operand fragments ----
-  f16x8 qf[KS];
+  // ---- Q fragments (B operand) ----
+  typedef typename std::conditional<QK_BF16, bf16x8, f16x8>::type qk_t;
+  qk_t qf[KS];
   {
     const int rc = row < S ? row : S - 1;
     const uint16_t* qrow = q + (((int64_t)b * Hq + h) * S + rc) * D;
@@ -99,10 +115,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * hl;
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      float x[8];
+      if constexpr (QK_BF16) {
+        qf[ks] = __builtin_bit_cast(bf16x8, w);
+      } else {
+        float x[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
-      if constexpr (ROPE) {
+        for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
         const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + rc) * (D / 2) + d0 / 2);
         const f32x4 c01 = tp[0], c23 = tp[1];
         const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
@@ -113,9 +131,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p] = x0 * c - x1 * s;
           x[2 * p + 1] = x0 * s + x1 * c;
         }
-      }
 #pragma unroll
-      for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * qscale);
+        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
+      }
     }
   }
 
@@ -127,42 +145,48 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const uint16_t* kg = k + kv_off;
   const uint16_t* vg = v + kv_off;
 
-  // staging registers for one tile
-  u32x4 kst[CPT], vst[CPT];
-  f32x4 tst[CPT][2];
-  auto issue_loads = [&](int k0) {
+  // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
+  // [(i * kWaves + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
+  // of row P / NCH.  Rows past S read row S-1 (finite data; those keys are masked).
+  auto direct_tile = [&](const uint16_t* src, uint16_t* dst_tile, int k0) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / NCH, cc = c % NCH;
-      const int key = k0 + r;
-      if (key < S) {
+    for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
+      const int base = (i * kWaves + wave) * 64;
+      const int P = base + lane;
+      const int r = P / NCH;
+      const int lc = swz<D>(r, P % NCH);
+      const int key = min(k0 + r, S - 1);
+      __builtin_amdgcn_global_load_lds(src + (int64_t)key * D + lc * 8,
+                                       (ATTN_LDS void*)(dst_tile + base * 8), 16, 0, 0);
+    }
+  };
+
+  // fused-mode staging (bf16 K + its coefficient rows)
+  u32x4 kst[KMODE == KMODE_FUSED ? CPT : 1];
+  f32x4 tst[KMODE == KMODE_FUSED ? CPT : 1][2];
+  auto fused_issue = [&](int k0) {
+    if constexpr (KMODE == KMODE_FUSED) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + kThreads * i;
+        const int r = c / NCH, cc = c % NCH;
+        const int key = min(k0 + r, S - 1);
         kst[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * D + cc * 8);
-        vst[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)key * D + cc * 8);
-        if constexpr (ROPE) {
-          const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + key) * (D / 2) + cc * 4);
-          tst[i][0] = tp[0];
-          tst[i][1] = tp[1];
-        }
-      } else {
-        kst[i] = u32x4{0, 0, 0, 0};
-        vst[i] = u32x4{0, 0, 0, 0};
-        if constexpr (ROPE) {
-          tst[i][0] = f32x4{1.f, 0.f, 1.f, 0.f};
-          tst[i][1] = f32x4{1.f, 0.f, 1.f, 0.f};
-        }
+        const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + key) * (D / 2) + cc * 4);
+        tst[i][0] = tp[0];
+        tst[i][1] = tp[1];
       }
     }
   };
-  auto store_tile = [&](int buf) {
+  auto fused_store = [&](int buf) {
+    if constexpr (KMODE == KMODE_FUSED) {
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / NCH, cc = c % NCH;
-      float x[8];
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + kThreads * i;
+        const int r = c / NCH, cc = c % NCH;
+        float x[8];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(kst[i][t]); x[2 * t + 1] = bf16hi(kst[i][t]); }
-      if constexpr (ROPE) {
+        for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(kst[i][t]); x[2 * t + 1] = bf16hi(kst[i][t]); }
         const float cs[8] = {tst[i][0][0], tst[i][0][1], tst[i][0][2], tst[i][0][3],
                              tst[i][1][0], tst[i][1][1], tst[i][1][2], tst[i][1][3]};
 #pragma unroll
@@ -172,14 +196,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p] = x0 * c - x1 * s;
           x[2 * p + 1] = x0 * s + x1 * c;
         }
-      }
-      u32x4 kh;
+        u32x4 kh;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kh[t] = pack_f16(x[2 * t], x[2 * t + 1]);
-      const int off = r * D + swz<D>(r, cc) * 8;
-      *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_lds[buf]) + off) = kh;
-      *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(v_lds[buf]) + off) = vst[i];
+        for (int t = 0; t < 4; ++t) kh[t] = pack_f16(x[2 * t], x[2 * t + 1]);
+        const int off = r * D + swz<D>(r, cc) * 8;
+        *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_lds[buf]) + off) = kh;
+      }
     }
+  };
+  auto issue_tile = [&](int k0, int buf) {
+    if constexpr (KMODE != KMODE_FUSED) direct_tile(kg, k_lds[buf], k0);
+    direct_tile(vg, v_lds[buf], k0);
   };
 
   // ---- accumulators ----
@@ -188,20 +215,23 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   for (int db = 0; db < DB; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;   // running row max of the exp2-domain scores
+  float l_run = 0.f;         // this lane's half of the row sum
 
-  // per-lane LDS read geometry
-  const int g16 = lane >> 4;     // 16-lane group
-  const int i16 = lane & 15;
-
-  issue_loads(0);
+  issue_tile(0, 0);
+  fused_issue(0);
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
     const int k0 = t * kBN;
-    store_tile(buf);
+    fused_store(buf);
+    // Each wave drains its own HBM->LDS loads of tile t (vmcnt is per wave), then the barrier
+    // makes every wave's part visible and guarantees every wave is done with tile t-1.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (t + 1 < n_tiles) issue_loads(k0 + kBN);
+    if (t + 1 < n_tiles) {
+      issue_tile(k0 + kBN, buf ^ 1);
+      fused_issue(k0 + kBN);
+    }
 
     if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_lds[buf]);
@@ -210,15 +240,28 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
         const int kr = kb * 32 + l32;
+        qk_t a[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
           const int off = kr * D + swz<D>(kr, 2 * ks + hl) * 8;
-          const f16x8 a = *reinterpret_cast<const ATTN_LDS f16x8*>(kb_lds + off);
-          sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, qf[ks], sacc[kb], 0, 0, 0);
+          a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>(kb_lds + off);
         }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          if constexpr (QK_BF16)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], sacc[kb], 0, 0, 0);
+          else
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], sacc[kb], 0, 0, 0);
+        }
+      }
+      if constexpr (QK_BF16) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sacc[kb][r] *= c_log2;
       }
       // mask (diagonal / tail tiles only)
       const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw) || (k0 + kBN > S);
@@ -268,12 +311,12 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       l_run += lsum;
       // O^T += V^T P^T
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 va[2][DB];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int db = 0; db < DB; ++db) {
-            bf16x8 a;
+          for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int tg = 0; tg < 2; ++tg) {
               const int vr = kb * 32 + 16 * s + 8 * tg + 4 * hl + (i16 >> 2);
@@ -283,10 +326,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                   reinterpret_cast<ATTN_LDS i16x4*>(const_cast<ATTN_LDS uint16_t*>(vb_lds) + off));
               const bf16x4 wb = __builtin_bit_cast(bf16x4, w);
 #pragma unroll
-              for (int e = 0; e < 4; ++e) a[4 * tg + e] = wb[e];
+              for (int e = 0; e < 4; ++e) va[s][db][4 * tg + e] = wb[e];
             }
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][s], oacc[db], 0, 0, 0);
-          }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[kb][s], oacc[db], 0, 0, 0);
+      }
     }
   }
 
@@ -312,38 +359,99 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         }
       }
     if (lse && hl == 0)
-      lse[((int64_t)b * Hq + h) * S + row] = (m_run + __log2f(l_tot)) * 0.6931471805599453f;
+      lse[((int64_t)b * Hq + h) * S + row] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
-template <int D, bool CAUSAL, bool ROPE, bool OUT_BF16>
-hipError_t go(const PrefillArgs& a, hipStream_t st) {
+// One pass over K: rotate every row at position pos0 + s (fp32 arithmetic, the same coefficient
+// table) and store it as fp16, the operand format of the Q.K^T product.
+template <int D>
+__global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restrict__ k,
+                                                         uint16_t* __restrict__ out, int64_t rows, int S,
+                                                         int pos0, const float2* __restrict__ table) {
+  constexpr int NCH = D / 8;
+  const int64_t n = rows * NCH;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / NCH;
+    const int cc = (int)(idx - r * NCH);
+    const int pos = pos0 + (int)(r % S);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(k + r * D + cc * 8);
+    const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)pos * (D / 2) + cc * 4);
+    const f32x4 c01 = tp[0], c23 = tp[1];
+    const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+    u32x4 hw;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf16lo(w[p]), x1 = bf16hi(w[p]);
+      const float c = cs[2 * p], s = cs[2 * p + 1];
+      hw[p] = pack_f16(x0 * c - x1 * s, x0 * s + x1 * c);
+    }
+    *reinterpret_cast<u32x4*>(out + r * D + cc * 8) = hw;
+  }
+}
+
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
+hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   const int nqb = (a.S + kBM - 1) / kBM;
   const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, ROPE, OUT_BF16>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)a.k,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16>), dim3((unsigned)blocks),
+                     dim3(kThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.pos0,
                      reinterpret_cast<const float2*>(a.table));
   return hipGetLastError();
 }
 
+template <int D, int KMODE>
+hipError_t dispatch_mode(const PrefillArgs& a, const void* kptr, hipStream_t st) {
+  if (a.causal)
+    return a.out_bf16 ? go<D, true, KMODE, true>(a, kptr, st) : go<D, true, KMODE, false>(a, kptr, st);
+  return a.out_bf16 ? go<D, false, KMODE, true>(a, kptr, st) : go<D, false, KMODE, false>(a, kptr, st);
+}
+
+template <int D>
+hipError_t rotate_keys(const void* k, void* k_rot, int64_t rows, int S, int pos0, const float* table,
+                       hipStream_t st) {
+  int64_t blocks = (rows * (D / 8) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(rope_k_f16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const uint16_t*)k, (uint16_t*)k_rot, rows, S, pos0,
+                     reinterpret_cast<const float2*>(table));
+  return hipGetLastError();
+}
+
 template <int D>
 hipError_t dispatch_d(const PrefillArgs& a, hipStream_t st) {
-  const bool rope = a.table != nullptr;
-  if (a.causal) {
-    if (rope) return a.out_bf16 ? go<D, true, true, true>(a, st) : go<D, true, true, false>(a, st);
-    return a.out_bf16 ? go<D, true, false, true>(a, st) : go<D, true, false, false>(a, st);
-  }
-  if (rope) return a.out_bf16 ? go<D, false, true, true>(a, st) : go<D, false, true, false>(a, st);
-  return a.out_bf16 ? go<D, false, false, true>(a, st) : go<D, false, false, false>(a, st);
+  if (!a.table) return dispatch_mode<D, KMODE_RAW>(a, a.k, st);
+  if (!a.workspace) return dispatch_mode<D, KMODE_FUSED>(a, a.k, st);
+  // one pass: rotated fp16 keys into the workspace, then the attention kernel streams them
+  const hipError_t e = rotate_keys<D>(a.k, a.workspace, (int64_t)a.B * a.Hkv * a.S, a.S, a.pos0, a.table, st);
+  if (e != hipSuccess) return e;
+  return dispatch_mode<D, KMODE_PREROT>(a, a.workspace, st);
 }
 
 }  // namespace
 
+size_t prefill_workspace_bytes(int B, int Hkv, int S, int D) {
+  return (size_t)B * Hkv * S * D * 2;
+}
+
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   return a.D == 64 ? dispatch_d<64>(a, st) : dispatch_d<128>(a, st);
+}
+
+hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
+                                  const float* table, hipStream_t st) {
+  const int64_t rows = (int64_t)B * Hkv * S;
+  return D == 64 ? rotate_keys<64>(k, k_rot, rows, S, pos0, table, st)
+                 : rotate_keys<128>(k, k_rot, rows, S, pos0, table, st);
+}
+
+hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st) {
+  return a.D == 64 ? dispatch_mode<64, KMODE_PREROT>(a, k_rot, st)
+                   : dispatch_mode<128, KMODE_PREROT>(a, k_rot, st);
 }
 
 }  // namespace attn

@@ -25,7 +25,10 @@ EXPORTED = (
     "attn_rope_table_bytes",
     "attn_rope_table_init",
     "attn_rope_apply",
+    "attn_prefill_workspace_bytes",
     "attn_prefill",
+    "attn_rotate_keys_f16",
+    "attn_prefill_prerotated",
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
@@ -54,9 +57,16 @@ def _load():
     lib.attn_rope_table_init.argtypes = [fp, i32, i32, ctypes.c_double, vp]
     lib.attn_rope_apply.restype = i32
     lib.attn_rope_apply.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, fp, i32, vp]
+    lib.attn_prefill_workspace_bytes.restype = sz
+    lib.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_prefill.restype = i32
     lib.attn_prefill.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
-                                 fp, i32, vp]
+                                 fp, i32, vp, sz, vp]
+    lib.attn_rotate_keys_f16.restype = i32
+    lib.attn_rotate_keys_f16.argtypes = [vp, vp, i32, i32, i32, i32, i32, fp, i32, vp]
+    lib.attn_prefill_prerotated.restype = i32
+    lib.attn_prefill_prerotated.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            fp, i32, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
@@ -151,9 +161,16 @@ def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.T
     return out
 
 
+def prefill_workspace_bytes(B, Hkv, S, D) -> int:
+    return int(_lib.attn_prefill_workspace_bytes(B, Hkv, S, D))
+
+
 def prefill(q, k, v, table=None, *, causal=True, pos0=0, out=None, out_dtype=None, lse=None,
-            stream=None):
-    """o = softmax(rope(q) rope(k)^T / sqrt(D)) v over [B, H, S, D] tensors (GQA when Hkv < Hq)."""
+            workspace=None, stream=None):
+    """o = softmax(rope(q) rope(k)^T / sqrt(D)) v over [B, H, S, D] tensors (GQA when Hkv < Hq).
+
+    workspace: optional uint8 GPU tensor of >= prefill_workspace_bytes() bytes; with it the keys
+    are rotated once into it (bf16 input with RoPE), without it the rotation is fused per tile."""
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
     B, Hq, S, D = q.shape
@@ -173,9 +190,53 @@ def prefill(q, k, v, table=None, *, causal=True, pos0=0, out=None, out_dtype=Non
     if table is not None:
         _need(table, "table")
         tmax = table.shape[0]
+    wsb = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        wsb = workspace.numel() * workspace.element_size()
     _check(_lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq,
-                             Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), tmax, _stream(stream)),
+                             Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), tmax, _ptr(workspace), wsb,
+                             _stream(stream)),
            "attn_prefill")
+    return out
+
+
+def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
+    """Rotated keys as fp16 (a torch.float16 tensor shaped like k), for prefill_prerotated."""
+    _need(k, "k")
+    _need(table, "table")
+    B, Hkv, S, D = k.shape
+    if k.dtype != torch.bfloat16:
+        raise TypeError("k must be bfloat16")
+    if out is None:
+        out = torch.empty(k.shape, dtype=torch.float16, device=k.device)
+    _need(out, "out")
+    if out.dtype != torch.float16 or out.shape != k.shape:
+        raise ValueError("out must be float16 shaped like k")
+    _check(_lib.attn_rotate_keys_f16(_ptr(k), _ptr(out), B, Hkv, S, D, pos0, _ptr(table), table.shape[0],
+                                     _stream(stream)), "attn_rotate_keys_f16")
+    return out
+
+
+def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, out=None, out_dtype=None, lse=None,
+                       stream=None):
+    """prefill() for keys already rotated by rotate_keys_f16 (same table and pos0)."""
+    for t, n in ((q, "q"), (k_rot, "k_rot"), (v, "v"), (table, "table")):
+        _need(t, n)
+    B, Hq, S, D = q.shape
+    Hkv = k_rot.shape[1]
+    if k_rot.dtype != torch.float16 or q.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q, v bfloat16 and k_rot float16 expected")
+    if k_rot.shape != (B, Hkv, S, D) or v.shape != k_rot.shape:
+        raise ValueError("k_rot and v must be [B, Hkv, S, D] matching q")
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    if lse is not None:
+        _need(lse, "lse")
+    _check(_lib.attn_prefill_prerotated(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(lse), _dt(out), B, Hq,
+                                        Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), table.shape[0],
+                                        _stream(stream)), "attn_prefill_prerotated")
     return out
 
 
