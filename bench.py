@@ -46,6 +46,8 @@ def parse():
     ap.add_argument("--long", action="store_true", help="also time the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "long", "all"], default="all")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -179,6 +181,13 @@ def main():
 
     W = inputs.WORKLOADS
     res = {}
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if args.only in ("prefill", "all"):
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
     if args.only in ("decode", "all"):

@@ -73,8 +73,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int CPT = kBN * NCH / kThreads;  // K chunks per thread (fused mode)
   constexpr bool QK_BF16 = KMODE == KMODE_RAW;
 
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][TILE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][TILE_ELEMS];
+  // Two stages, as four distinct LDS objects: with the stage fixed at compile time (the key loop
+  // is unrolled by two) the compiler can see that the HBM->LDS loads of the next tile never
+  // alias the current tile's operand reads, so it does not wait for them before reading.
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE_ELEMS];
 
   // ---- workgroup -> (query block, batch, head) ----
   const int G = Hq / Hkv;
@@ -94,7 +99,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = wave_uniform(tid >> 6);
   const int hl = lane >> 5;      // which half of the wave
   const int l32 = lane & 31;
   const int g16 = lane >> 4;     // 16-lane group
@@ -147,19 +152,58 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
   // [(i * kWaves + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
-  // of row P / NCH.  Rows past S read row S-1 (finite data; those keys are masked).
-  auto direct_tile = [&](const uint16_t* src, uint16_t* dst_tile, int k0) {
+  // of row P / NCH.  The per-lane element offsets are fixed for the whole kernel; each tile adds
+  // a wave-uniform base.  Rows past S read row S-1 (finite data; those keys are masked).
+  // Byte offsets are unsigned 32-bit so the loads use the scalar-base + vector-offset form.
+  uint32_t dma_byte[DIRECT_PER_WAVE];
+  int dma_row[DIRECT_PER_WAVE];
 #pragma unroll
-    for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
-      const int base = (i * kWaves + wave) * 64;
-      const int P = base + lane;
-      const int r = P / NCH;
-      const int lc = swz<D>(r, P % NCH);
-      const int key = min(k0 + r, S - 1);
-      __builtin_amdgcn_global_load_lds(src + (int64_t)key * D + lc * 8,
-                                       (ATTN_LDS void*)(dst_tile + base * 8), 16, 0, 0);
+  for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
+    const int P = (i * kWaves + wave) * 64 + lane;
+    const int r = P / NCH;
+    dma_row[i] = r;
+    dma_byte[i] = (uint32_t)(r * D + swz<D>(r, P % NCH) * 8) * 2u;
+  }
+  auto direct_tile = [&](const uint16_t* src, uint16_t* dst_tile, int k0) {
+    // (operands are formed in locals first: the host compilation pass rejects captured-array
+    // elements inside the builtin's argument list and would silently drop the kernel)
+    const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * D);
+    if (k0 + kBN <= S) {
+#pragma unroll
+      for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
+        const uint32_t off = dma_byte[i];
+        const void* g = base + off;
+        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * kWaves + wave) * 512);
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
+        const int r = dma_row[i];
+        const int rr = min(r, S - 1 - k0);
+        const uint32_t off = dma_byte[i] - (uint32_t)((r - rr) * D * 2);
+        const void* g = base + off;
+        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * kWaves + wave) * 512);
+        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+      }
     }
   };
+  // Per-lane LDS operand offsets (bytes).  K operand (ds_read_b128): row kb*32 + l32, logical
+  // chunk 2*ks + hl.  V^T operand (ds_read_b64_tr_b16): row kb*32 + 16*s + 8*tg + 4*hl + i16/4,
+  // logical chunk 4*db + 2*(g16&1) + (i16&3)/2, half-chunk i16&1.  The swizzle only sees the low
+  // four row bits, which kb and s do not change, so those enter as immediate offsets.
+  int kaddr[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = (l32 * D + swz<D>(l32, 2 * ks + hl) * 8) * 2;
+  int vaddr[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; ++db)
+#pragma unroll
+    for (int tg = 0; tg < 2; ++tg) {
+      const int vr = 8 * tg + 4 * hl + (i16 >> 2);
+      const int lc = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
+      vaddr[db][tg] = (vr * D + swz<D>(vr, lc) * 8 + 4 * (i16 & 1)) * 2;
+    }
 
   // fused-mode staging (bf16 K + its coefficient rows)
   u32x4 kst[KMODE == KMODE_FUSED ? CPT : 1];
@@ -178,7 +222,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       }
     }
   };
-  auto fused_store = [&](int buf) {
+  auto fused_store = [&](uint16_t* k_tile) {
     if constexpr (KMODE == KMODE_FUSED) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
@@ -200,13 +244,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
         for (int t = 0; t < 4; ++t) kh[t] = pack_f16(x[2 * t], x[2 * t + 1]);
         const int off = r * D + swz<D>(r, cc) * 8;
-        *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_lds[buf]) + off) = kh;
+        *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_tile) + off) = kh;
       }
     }
   };
-  auto issue_tile = [&](int k0, int buf) {
-    if constexpr (KMODE != KMODE_FUSED) direct_tile(kg, k_lds[buf], k0);
-    direct_tile(vg, v_lds[buf], k0);
+  auto issue_tile = [&](int k0, uint16_t* k_tile, uint16_t* v_tile) {
+    if constexpr (KMODE != KMODE_FUSED) direct_tile(kg, k_tile, k0);
+    direct_tile(vg, v_tile, k0);
   };
 
   // ---- accumulators ----
@@ -218,35 +262,33 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   float m_run = -INFINITY;   // running row max of the exp2-domain scores
   float l_run = 0.f;         // this lane's half of the row sum
 
-  issue_tile(0, 0);
-  fused_issue(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int buf = t & 1;
+  // One key tile: t is the tile index; the stage (and so every LDS address) is fixed at compile
+  // time by STAGE.
+  auto tile_step = [&](auto stage_c, int t) {
+    constexpr int STAGE = decltype(stage_c)::value;
+    uint16_t* k_cur = STAGE ? k_lds1 : k_lds0;
+    uint16_t* v_cur = STAGE ? v_lds1 : v_lds0;
+    uint16_t* k_nxt = STAGE ? k_lds0 : k_lds1;
+    uint16_t* v_nxt = STAGE ? v_lds0 : v_lds1;
     const int k0 = t * kBN;
-    fused_store(buf);
+    fused_store(k_cur);
     // Each wave drains its own HBM->LDS loads of tile t (vmcnt is per wave), then the barrier
     // makes every wave's part visible and guarantees every wave is done with tile t-1.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      issue_tile(k0 + kBN, buf ^ 1);
-      fused_issue(k0 + kBN);
-    }
+    if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
 
     if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
-      const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_lds[buf]);
-      const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_lds[buf]);
+      const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
+      const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
       // S^T = K Q^T for two 32-key blocks
       f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int kr = kb * 32 + l32;
         qk_t a[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int off = kr * D + swz<D>(kr, 2 * ks + hl) * 8;
-          a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>(kb_lds + off);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>((const ATTN_LDS char*)kb_lds + kaddr[ks] + kb * 32 * D * 2);
 #pragma unroll
         for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
@@ -292,22 +334,25 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
         m_run = m_new;
       }
-      // p = 2^(s - m), packed to bf16 as the B operand of P.V
+      // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
+      // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
       bf16x8 pf[2][2];
       float lsum = 0.f;
+      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          float p[8];
+        for (int s = 0; s < 2; ++s)
 #pragma unroll
-          for (int tt = 0; tt < 8; ++tt) {
-            p[tt] = fast_exp2(sacc[kb][8 * s + tt] - m_run);
-            lsum += p[tt];
+          for (int tt = 0; tt < 8; tt += 2) {
+            bf16x2 pp;
+            pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt] - m_run);
+            pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1] - m_run);
+            pf[kb][s][tt] = pp[0];
+            pf[kb][s][tt + 1] = pp[1];
+            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
           }
-#pragma unroll
-          for (int tt = 0; tt < 8; ++tt) pf[kb][s][tt] = (__bf16)p[tt];
-        }
       l_run += lsum;
       // O^T += V^T P^T
 #pragma unroll
@@ -319,11 +364,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int tg = 0; tg < 2; ++tg) {
-              const int vr = kb * 32 + 16 * s + 8 * tg + 4 * hl + (i16 >> 2);
-              const int lc = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
-              const int off = vr * D + swz<D>(vr, lc) * 8 + 4 * (i16 & 1);
-              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                  reinterpret_cast<ATTN_LDS i16x4*>(const_cast<ATTN_LDS uint16_t*>(vb_lds) + off));
+              ATTN_LDS i16x4* pa = reinterpret_cast<ATTN_LDS i16x4*>(
+                  (ATTN_LDS char*)(const_cast<ATTN_LDS uint16_t*>(vb_lds)) + vaddr[db][tg] +
+                  (kb * 32 + 16 * s) * D * 2);
+              const i16x4 w = __builtin_amdgcn_ds_read_tr16_b64_v4i16(pa);
               const bf16x4 wb = __builtin_bit_cast(bf16x4, w);
 #pragma unroll
               for (int e = 0; e < 4; ++e) va[s][db][4 * tg + e] = wb[e];
@@ -335,6 +379,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[kb][s], oacc[db], 0, 0, 0);
       }
     }
+    // Fused RoPE: the next tile's keys and coefficients are fetched only now, so the staging
+    // registers are not live across the tile's MFMA work (no spills); the other workgroup on the
+    // CU covers the load latency.
+    if (t + 1 < n_tiles) fused_issue(k0 + kBN);
+  };
+
+  issue_tile(0, k_lds0, v_lds0);
+  fused_issue(0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    tile_step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // ---- finalize ----
