@@ -41,7 +41,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kRowsPerWave = 32;
-constexpr int kBM = kWaves * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kRowBlocks = 1;               // 32-row blocks per wave on the streaming paths
 constexpr int kBN = 64;                     // keys per tile
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kNumXcd = 8;
@@ -59,8 +59,8 @@ __device__ __forceinline__ int swz(int r, int lc) {
   }
 }
 
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int RB>
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int S, int pos0,
@@ -72,6 +72,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   constexpr int DIRECT_PER_WAVE = TILE_ELEMS * 2 / 1024 / kWaves;  // 1 KB wave-loads per tensor
   constexpr int CPT = kBN * NCH / kThreads;  // K chunks per thread (fused mode)
   constexpr bool QK_BF16 = KMODE == KMODE_RAW;
+  constexpr int ROWS = kRowsPerWave * RB;    // query rows per wave
+  constexpr int BM = kWaves * ROWS;          // query rows per workgroup
 
   // Two stages, as four distinct LDS objects: with the stage fixed at compile time (the key loop
   // is unrolled by two) the compiler can see that the HBM->LDS loads of the next tile never
@@ -83,7 +85,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   // ---- workgroup -> (query block, batch, head) ----
   const int G = Hq / Hkv;
-  const int nqb = (S + kBM - 1) / kBM;
+  const int nqb = (S + BM - 1) / BM;
   const int NG = nqb * B * Hkv;
   const int id = blockIdx.x;
   const int xcd = id % kNumXcd;
@@ -104,24 +106,27 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int l32 = lane & 31;
   const int g16 = lane >> 4;     // 16-lane group
   const int i16 = lane & 15;
-  const int q0 = qblock * kBM;
-  const int qw = q0 + wave * kRowsPerWave;  // first row of this wave
-  const int row = qw + l32;                 // this lane's query row
+  const int q0 = qblock * BM;
+  const int qw = q0 + wave * ROWS;          // first row of this wave
+  int row[RB];                              // this lane's query row in each row block
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) row[rb] = qw + 32 * rb + l32;
   // exp2 argument scale: folded into Q (fp16 modes) or applied to raw scores (bf16 mode)
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
 
   // ---- Q fragments (B operand) ----
   typedef typename std::conditional<QK_BF16, bf16x8, f16x8>::type qk_t;
-  qk_t qf[KS];
-  {
-    const int rc = row < S ? row : S - 1;
+  qk_t qf[RB][KS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int rc = row[rb] < S ? row[rb] : S - 1;
     const uint16_t* qrow = q + (((int64_t)b * Hq + h) * S + rc) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * hl;
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
       if constexpr (QK_BF16) {
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
+        qf[rb][ks] = __builtin_bit_cast(bf16x8, w);
       } else {
         float x[8];
 #pragma unroll
@@ -137,19 +142,18 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p + 1] = x0 * s + x1 * c;
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
+        for (int t = 0; t < 8; ++t) qf[rb][ks][t] = (_Float16)(x[t] * c_log2);
       }
     }
   }
 
   // ---- key range ----
-  const int q_last = min(q0 + kBM, S) - 1;
+  const int q_last = min(q0 + BM, S) - 1;
   const int key_end = CAUSAL ? q_last + 1 : S;
   const int n_tiles = (key_end + kBN - 1) / kBN;
   const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S * D;
   const uint16_t* kg = k + kv_off;
   const uint16_t* vg = v + kv_off;
-
   // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
   // [(i * kWaves + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
   // of row P / NCH.  The per-lane element offsets are fixed for the whole kernel; each tile adds
@@ -254,13 +258,22 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   };
 
   // ---- accumulators ----
-  f32x16 oacc[DB];
+  f32x16 oacc[RB][DB];
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-  float m_run = -INFINITY;   // running row max of the exp2-domain scores
-  float l_run = 0.f;         // this lane's half of the row sum
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
+  float m_run[RB];   // running row max of the exp2-domain scores
+  float l_run[RB];   // this lane's half of the row sum
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.f;
+  }
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
   // One key tile: t is the tile index; the stage (and so every LDS address) is fixed at compile
   // time by STAGE.
@@ -278,11 +291,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
 
-    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
+    if (!CAUSAL || k0 <= qw + ROWS - 1) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
       const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
-      // S^T = K Q^T for two 32-key blocks
-      f32x16 sacc[2];
+      // S^T = K Q^T for two 32-key blocks; each K fragment feeds every row block
+      f32x16 sacc[RB][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         qk_t a[KS];
@@ -290,71 +303,76 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         for (int ks = 0; ks < KS; ++ks)
           a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>((const ATTN_LDS char*)kb_lds + kaddr[ks] + kb * 32 * D * 2);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+        for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          if constexpr (QK_BF16)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], sacc[kb], 0, 0, 0);
-          else
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], sacc[kb], 0, 0, 0);
+          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if constexpr (QK_BF16)
+              sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[rb][ks], sacc[rb][kb], 0, 0, 0);
+            else
+              sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[rb][ks], sacc[rb][kb], 0, 0, 0);
+          }
+      }
+      bf16x8 pf[RB][2][2];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb) {
+        if constexpr (QK_BF16) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[rb][kb][r] *= c_log2;
         }
-      }
-      if constexpr (QK_BF16) {
+        // mask (diagonal / tail tiles only)
+        const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw + 32 * rb) || (k0 + kBN > S);
+        if (need_mask) {
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+              if ((CAUSAL && key > row[rb]) || key >= S) sacc[rb][kb][r] = -INFINITY;
+            }
+        }
+        // row max over this tile
+        float mx = sacc[rb][0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[rb][0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][1][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_new = fmaxf(m_run[rb], mx);
+        const bool need = m_new > m_run[rb] + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float alpha = fast_exp2(m_run[rb] - m_new);
+          l_run[rb] *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
+          m_run[rb] = m_new;
+        }
+        // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
+        // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
+        float lsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[kb][r] *= c_log2;
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tt = 0; tt < 8; tt += 2) {
+              bf16x2 pp;
+              pp[0] = (__bf16)fast_exp2(sacc[rb][kb][8 * s + tt] - m_run[rb]);
+              pp[1] = (__bf16)fast_exp2(sacc[rb][kb][8 * s + tt + 1] - m_run[rb]);
+              pf[rb][kb][s][tt] = pp[0];
+              pf[rb][kb][s][tt + 1] = pp[1];
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+            }
+        l_run[rb] += lsum;
       }
-      // mask (diagonal / tail tiles only)
-      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw) || (k0 + kBN > S);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if ((CAUSAL && key > row) || key >= S) sacc[kb][r] = -INFINITY;
-          }
-      }
-      // row max over this tile
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-      mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const bool need = m_new > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(need) != 0) {
-        const float alpha = fast_exp2(m_run - m_new);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-        m_run = m_new;
-      }
-      // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
-      // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
-      bf16x8 pf[2][2];
-      float lsum = 0.f;
-      typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-      const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-          for (int tt = 0; tt < 8; tt += 2) {
-            bf16x2 pp;
-            pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt] - m_run);
-            pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1] - m_run);
-            pf[kb][s][tt] = pp[0];
-            pf[kb][s][tt + 1] = pp[1];
-            lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-          }
-      l_run += lsum;
-      // O^T += V^T P^T
+      // O^T += V^T P^T; each V^T fragment feeds every row block
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         bf16x8 va[2][DB];
@@ -376,7 +394,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[kb][s], oacc[db], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[rb][kb][s], oacc[rb][db], 0, 0, 0);
       }
     }
     // Fused RoPE: the next tile's keys and coefficients are fetched only now, so the staging
@@ -393,28 +413,31 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 
   // ---- finalize ----
-  const float l_tot = l_run + swap_halves(l_run);
-  if (row < S) {
-    const float inv = 1.0f / l_tot;
-    const int64_t orow = (((int64_t)b * Hq + h) * S + row) * D;
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+  for (int rb = 0; rb < RB; ++rb) {
+    const float l_tot = l_run[rb] + swap_halves(l_run[rb]);
+    if (row[rb] < S) {
+      const float inv = 1.0f / l_tot;
+      const int64_t orow = (((int64_t)b * Hq + h) * S + row[rb]) * D;
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const int d0 = db * 32 + 8 * r4 + 4 * hl;
-        const float o0 = oacc[db][4 * r4 + 0] * inv, o1 = oacc[db][4 * r4 + 1] * inv;
-        const float o2 = oacc[db][4 * r4 + 2] * inv, o3 = oacc[db][4 * r4 + 3] * inv;
-        if constexpr (OUT_BF16) {
-          u32x2 w;
-          w[0] = pack_bf16(o0, o1);
-          w[1] = pack_bf16(o2, o3);
-          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o) + orow + d0) = w;
-        } else {
-          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = db * 32 + 8 * r4 + 4 * hl;
+          const float o0 = oacc[rb][db][4 * r4 + 0] * inv, o1 = oacc[rb][db][4 * r4 + 1] * inv;
+          const float o2 = oacc[rb][db][4 * r4 + 2] * inv, o3 = oacc[rb][db][4 * r4 + 3] * inv;
+          if constexpr (OUT_BF16) {
+            u32x2 w;
+            w[0] = pack_bf16(o0, o1);
+            w[1] = pack_bf16(o2, o3);
+            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o) + orow + d0) = w;
+          } else {
+            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
+          }
         }
-      }
-    if (lse && hl == 0)
-      lse[((int64_t)b * Hq + h) * S + row] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+      if (lse && hl == 0)
+        lse[((int64_t)b * Hq + h) * S + row[rb]] = (m_run[rb] + log2f(l_tot)) * 0.6931471805599453f;
+    }
   }
 }
 
@@ -446,13 +469,20 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
   }
 }
 
+// Row blocks per wave: two (64 query rows per wave, one wave per SIMD) on the streaming paths,
+// one for the fused-RoPE path, whose staged key registers would not fit beside two blocks.
+template <int KMODE>
+constexpr int row_blocks() { return KMODE == KMODE_FUSED ? 1 : kRowBlocks; }
+
 template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
 hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
+  constexpr int RB = row_blocks<KMODE>();
+  constexpr int BM = kWaves * kRowsPerWave * RB;
   const int G = a.Hq / a.Hkv;
-  const int nqb = (a.S + kBM - 1) / kBM;
+  const int nqb = (a.S + BM - 1) / BM;
   const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, RB>), dim3((unsigned)blocks),
                      dim3(kThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.pos0,
                      reinterpret_cast<const float2*>(a.table));
