@@ -1,24 +1,33 @@
 """Benchmark of the RoPE + causal GQA attention path on one MI355X.
 
 One step = one pass of the hot path over the workload's synthetic batch:
-  * prefill (headline): the GQA workload at full size -- B=1, Hq=64, Hkv=8, S=8192, D=128,
-    bf16 inputs, causal, RoPE base 10000 fused into the Q/K tile loads; one attn_prefill launch;
-  * decode: batch 32 against an 8192-token cache, Hq=64, Hkv=8, D=128, query rotated at 8192;
-    one attn_decode call (split + merge launches);
-  * long (optional, --long): the 32k-token prefill with 1% of keys scaled by 8.
+  * prefill (headline ``value``): the GQA workload at full size -- B=1, Hq=64, Hkv=8, S=8192,
+    D=128, bf16 inputs, causal, RoPE base 10000 on Q and K.  A step is the two launches that
+    attn_prefill makes when it is given a workspace: the keys are rotated once into fp16
+    (rotate_keys_f16), then the attention kernel rotates each Q tile as it loads it and streams
+    the rotated keys.  They are issued here through the two-stage entry points so that HIP events
+    can bracket the attention kernel inside the timed region; attn_prefill enqueues exactly the
+    same two kernels (a GPU test checks that both routes give identical bytes).
+  * decode (sub-object ``decode``): batch 32 against an 8192-token cache, Hq=64, Hkv=8, D=128,
+    query rotated at position 8192; one attn_decode call (split + merge launches).
+  * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
+    key rows scaled by 8.
 
-Inputs are resident in HBM before timing starts.  Warmup launches, then K timed launches
-bracketed by torch.cuda.synchronize(), timed with HIP events recorded on the stream the
-library launches on (torch's current stream).  Prints ONE JSON line on stdout.
+Inputs are resident in HBM before timing starts.  W untimed warmup steps, then K timed steps
+bracketed by torch.cuda.synchronize(), timed with HIP events recorded on the stream the library
+launches on (torch's current stream).  Prints ONE JSON line on stdout.
 
-``value`` is prefill TFLOP/s with FLOPs = 2*B*Hq*S^2*D (the causal half of QK^T and PV).
-The decode figure is K/V bytes read (2*B*Hkv*L*D*2 = 1 GiB) per second.  ``cpu_baseline``
-times the fp64 oracle on a bounded sample of query rows of the same workload on the host.
+``value`` is prefill TFLOP/s with FLOPs = 2*B*Hq*S^2*D (the causal half of QK^T and PV).  The
+decode figure is K/V bytes read (2*B*Hkv*L*D*2 = 1 GiB) per second.  ``roofline`` is for the
+dominant kernel (the prefill attention kernel): algorithmic FLOPs per launch / its mean launch
+duration, against the dense bf16 matrix peak.  ``cpu_baseline`` times the fp64 oracle on a bounded
+sample of query rows of the same workload on the host.
 """
 
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -26,24 +35,57 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 MFMA_BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16/fp16 matrix peak
 HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 
-# HBM bytes measured by rocprofv3 --pmc (FETCH_SIZE / WRITE_SIZE per dispatch, scaled by the
-# copy-kernel calibration factor); None until counters are taken for the current kernels.
-MEASURED_TRAFFIC = {"prefill_gqa": None, "decode": None}
+# HBM bytes per launch from rocprofv3 --pmc (FETCH_SIZE and WRITE_SIZE in KiB per dispatch,
+# each divided by what the same counter reads per byte for a plain 1 GiB device copy), and the
+# SHA-256 of the kernel sources they were taken on.  The figure is reported only while the
+# sources are unchanged; otherwise the kernel changed since the counters were taken -> null.
+# Calibration (1 GiB device-to-device copy, __amd_rocclr_copyBuffer): FETCH_SIZE reads 524302 KiB
+# for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
+MEASURED_TRAFFIC = {
+    # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
+    # FETCH_SIZE 159360.2 KiB, WRITE_SIZE 131072.1 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 460587520, "sources_sha256_16": "0323c28bb296fea3"},
+    # decode_split_kernel + decode_merge_kernel, B=32 L=8192 Hq=64 Hkv=8 D=128, n_split 2 (4 each):
+    # FETCH_SIZE 525265.1 + 1159.5 KiB, WRITE_SIZE 2112.0 + 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1080804557, "sources_sha256_16": "c345e9745862076f"},
+}
+KERNEL_SOURCES = {
+    "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
+                    "transformer_self_attention_amd/csrc/common.h"],
+    "decode": ["transformer_self_attention_amd/csrc/decode.hip",
+               "transformer_self_attention_amd/csrc/common.h"],
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def sources_digest(key):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[key]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic(key):
+    m = MEASURED_TRAFFIC.get(key)
+    if not m or m.get("sources_sha256_16") != sources_digest(key):
+        return None
+    return m["bytes_per_launch"]
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--long", action="store_true", help="also time the 32k long-context prefill")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["prefill", "decode", "long", "all"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -51,7 +93,13 @@ def parse():
     return ap.parse_args()
 
 
-def time_launches(fn, steps, warmup):
+def _stats(xs):
+    xs = sorted(xs)
+    return {"mean": sum(xs) / len(xs), "median": xs[len(xs) // 2], "min": xs[0]}
+
+
+def time_calls(fn, steps, warmup):
+    """Mean ms per call of fn over `steps` back-to-back calls (events on torch's current stream)."""
     import torch
     for _ in range(warmup):
         fn()
@@ -64,12 +112,10 @@ def time_launches(fn, steps, warmup):
         fn()
     e1.record(stream)
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps   # ms per call
+    return e0.elapsed_time(e1) / steps
 
 
 def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
-    """Times one prefill step (keys rotated once into a workspace + the attention kernel), and
-    separately the attention kernel alone, the key-rotation pass alone and the fused variant."""
     import torch
     log(f"[bench] generating {wl.name} prefill inputs B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} S={wl.S} D={wl.D}")
     p = inputs.make_prefill(wl)
@@ -80,17 +126,42 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
     krot = ws.view(torch.float16).view(k.shape)
     torch.cuda.synchronize()
     flops = wl.prefill_flops()
+
+    def step():
+        lib.rotate_keys_f16(k, tab, out=krot)
+        lib.prefill_prerotated(q, krot, v, tab, out=out)
+
     log(f"[bench] timing {wl.name} prefill step: warmup {warmup}, steps {steps}")
-    r = {"p": p}
-    r["ms_step"] = time_launches(lambda: lib.prefill(q, k, v, tab, out=out, workspace=ws), steps, warmup)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    start, end = ev(), ev()
+    marks = [(ev(), ev(), ev()) for _ in range(steps)]
+    start.record(stream)
+    for a, b, c in marks:
+        a.record(stream)
+        lib.rotate_keys_f16(k, tab, out=krot)
+        b.record(stream)
+        lib.prefill_prerotated(q, krot, v, tab, out=out)
+        c.record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    r = {"p": p, "ms_step": start.elapsed_time(end) / steps,
+         "kernel_ms": _stats([b.elapsed_time(c) for _, b, c in marks]),
+         "rotate_ms": _stats([a.elapsed_time(b) for a, b, _ in marks])}
+    r["tflops_step"] = flops / (r["ms_step"] * 1e-3) / 1e12
+    r["tflops_kernel"] = flops / (r["kernel_ms"]["mean"] * 1e-3) / 1e12
     if variants:
-        r["ms_kernel"] = time_launches(lambda: lib.prefill_prerotated(q, krot, v, tab, out=out), steps, warmup)
-        r["ms_rope"] = time_launches(lambda: lib.rotate_keys_f16(k, tab, out=krot), steps, warmup)
-        r["ms_fused"] = time_launches(lambda: lib.prefill(q, k, v, tab, out=out), steps, warmup)
-    for key in ("ms_step", "ms_kernel", "ms_fused"):
-        if key in r:
-            r[key.replace("ms_", "tflops_")] = flops / (r[key] * 1e-3) / 1e12
-    log(f"[bench] {wl.name} prefill: " + ", ".join(f"{k_}={v_:.4f}" for k_, v_ in r.items() if k_ != "p"))
+        # the same step through the one-call entry point, and the variant without a workspace
+        # (key rotation fused into every K tile load)
+        r["ms_one_call"] = time_calls(lambda: lib.prefill(q, k, v, tab, out=out, workspace=ws), steps, warmup)
+        r["ms_fused"] = time_calls(lambda: lib.prefill(q, k, v, tab, out=out), steps, warmup)
+        r["tflops_fused"] = flops / (r["ms_fused"] * 1e-3) / 1e12
+    log(f"[bench] {wl.name} prefill: step {r['ms_step']:.4f} ms ({r['tflops_step']:.1f} TFLOP/s), "
+        f"attention kernel mean {r['kernel_ms']['mean']:.4f} ms ({r['tflops_kernel']:.1f} TFLOP/s), "
+        f"key rotation {r['rotate_ms']['mean']:.4f} ms")
     return r
 
 
@@ -107,11 +178,14 @@ def bench_decode(lib, inputs, wl, steps, warmup):
                      device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] timing decode: warmup {warmup}, steps {steps}")
-    ms = time_launches(lambda: lib.decode(q, kc, vc, cl, qp, tab, out=out, workspace=ws), steps, warmup)
+    # One step is one attn_decode call (its split and merge launches back to back); the steps are
+    # timed as a whole, without events between them.
+    ms = time_calls(lambda: lib.decode(q, kc, vc, cl, qp, tab, out=out, workspace=ws), steps, warmup)
     nbytes = wl.decode_kv_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
-    log(f"[bench] decode: {ms:.4f} ms/call, {gbs:.1f} GB/s of K/V")
-    return d, ms, gbs
+    log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
+    n_split = lib.decode_num_splits(wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, 0)
+    return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split}
 
 
 def cpu_threads():
@@ -123,7 +197,7 @@ def cpu_threads():
     return int(n)
 
 
-def cpu_baseline_prefill(p, target_s=12.0):
+def cpu_baseline_prefill(p, target_s=16.0):
     """Time the fp64 oracle on seeded query rows of the same workload (all heads)."""
     import oracle
     wl = p.wl
@@ -144,9 +218,11 @@ def cpu_baseline_prefill(p, target_s=12.0):
     tflops = flops / dt / 1e12
     return {"value": tflops, "unit": "TFLOP/s", "cores": cpu_threads(), "kind": "oracle",
             "sample": f"{n} seeded query rows per head x {wl.Hq} heads of the {wl.name} workload "
-                      f"(S={wl.S}), fp64 NumPy, {dt:.2f} s wall; FLOPs counted as 4*D*(i+1) per row",
+                      f"(S={wl.S}), fp64 NumPy, {dt:.2f} s wall; FLOPs counted as 4*D*(i+1) per row "
+                      f"(the oracle also materialises the masked half of each score row)",
             "wall_s": dt, "host_cpu_count": os.cpu_count(),
-            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None}
+            "affinity": len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+            "full_config_extrapolation_s": dt * wl.prefill_flops() / flops}
 
 
 def cpu_baseline_decode(d, target_s=6.0):
@@ -170,8 +246,8 @@ def cpu_baseline_decode(d, target_s=6.0):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see the sharding notes in the design document); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: this library has no multi-GPU path "
+              "(the sharding plan is written up in the design notes); use --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -192,8 +268,8 @@ def main():
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], args.steps, args.warmup)
-    if args.long or args.only == "long":
-        res["long"] = bench_prefill(lib, inputs, W["long"], max(2, args.steps // 4), min(args.warmup, 2),
+    if args.only == "long" or (args.only == "all" and not args.no_long):
+        res["long"] = bench_prefill(lib, inputs, W["long"], max(3, args.steps // 5), max(2, args.warmup // 5),
                                     variants=False)
 
     out = {
@@ -204,52 +280,60 @@ def main():
     }
     if "prefill" in res:
         r = res["prefill"]
-        p, ms, tflops = r["p"], r["ms_step"], r["tflops_step"]
-        kern_tflops = r.get("tflops_kernel", tflops)
-        wl = p.wl
+        wl = r["p"].wl
+        kt = r["tflops_kernel"]
         out.update({
-            "value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 5),
-            "step_parts": {"rotate_keys_f16_ms": round(r.get("ms_rope", float("nan")), 5),
-                           "attention_kernel_ms": round(r.get("ms_kernel", float("nan")), 5),
+            "value": round(r["tflops_step"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_step"], 5),
+            "step_parts": {"rotate_keys_f16_ms": {k_: round(v_, 5) for k_, v_ in r["rotate_ms"].items()},
+                           "attention_kernel_ms": {k_: round(v_, 5) for k_, v_ in r["kernel_ms"].items()},
+                           "attn_prefill_one_call_ms": round(r.get("ms_one_call", float("nan")), 5),
                            "fused_rope_variant_ms": round(r.get("ms_fused", float("nan")), 5),
                            "fused_rope_variant_tflops": round(r.get("tflops_fused", float("nan")), 2)},
             "operand_dtypes": {"inputs": "bf16", "qk_mfma": "f16", "pv_mfma": "bf16", "accumulate": "f32",
                                "output": "bf16"},
-            "config": {"workload": "GQA causal prefill with fused RoPE", "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv,
-                       "seq_len": wl.S, "head_dim": wl.D, "causal": True, "rope_base": wl.rope_base,
-                       "flops_per_step": wl.prefill_flops()},
-            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated keys)",
-                         "achieved": round(kern_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(kern_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                         "traffic": MEASURED_TRAFFIC["prefill_gqa"]},
+            "config": {"workload": "GQA causal prefill with RoPE on Q and K", "B": wl.B, "Hq": wl.Hq,
+                       "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D, "causal": True,
+                       "rope_base": wl.rope_base, "flops_per_step": wl.prefill_flops()},
+            "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated fp16 keys)",
+                         "achieved": round(kt, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(kt / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "traffic": traffic("prefill_gqa"),
+                         "flops_per_launch": wl.prefill_flops(),
+                         "algorithmic_bytes_per_launch": wl.prefill_bytes()},
         })
     if "decode" in res:
-        d, ms, gbs = res["decode"]
-        wl = d.wl
-        dec = {"metric": "decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s", "ms_per_step": round(ms, 5),
+        r = res["decode"]
+        wl = r["d"].wl
+        gbs = r["gbs"]
+        dec = {"metric": "decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
+               "ms_per_step": round(r["ms"], 5),
                "config": {"workload": "batch decode against a KV cache", "B": wl.B, "cache_len": wl.S,
-                          "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D, "kv_bytes_per_step": wl.decode_kv_bytes()},
+                          "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D, "n_split": r["n_split"],
+                          "kv_bytes_per_step": wl.decode_kv_bytes()},
                "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": MEASURED_TRAFFIC["decode"]}}
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode")}}
         if "prefill" not in res:
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"],
                         "config": dec["config"], "roofline": dec["roofline"]})
         out["decode"] = dec
     if "long" in res:
         r = res["long"]
-        p, ms, tflops = r["p"], r["ms_step"], r["tflops_step"]
-        out["long_prefill"] = {"value": round(tflops, 2), "unit": "TFLOP/s", "ms_per_step": round(ms, 4),
-                               "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                               "config": {"B": p.wl.B, "Hq": p.wl.Hq, "Hkv": p.wl.Hkv, "seq_len": p.wl.S,
-                                          "head_dim": p.wl.D, "big_key_frac": p.wl.big_key_frac}}
+        wl = r["p"].wl
+        out["long_prefill"] = {
+            "value": round(r["tflops_step"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_step"], 4),
+            "frac": round(r["tflops_step"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attention_kernel_tflops": round(r["tflops_kernel"], 2),
+            "attention_kernel_frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
+                       "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale}}
     if not args.no_cpu_baseline:
         if "prefill" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, prefill sample)")
             out["cpu_baseline"] = cpu_baseline_prefill(res["prefill"]["p"])
         if "decode" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, decode sample)")
-            cb = cpu_baseline_decode(res["decode"][0])
+            cb = cpu_baseline_decode(res["decode"]["d"])
             if "prefill" in res:
                 out["decode"]["cpu_baseline"] = cb
             else:

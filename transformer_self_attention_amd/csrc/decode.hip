@@ -9,7 +9,8 @@
 //
 // Pass 1 (decode_split_kernel), one workgroup per (sequence, KV head, split):
 //  * 4 waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
-//    flight while sub-block i is consumed (16 x 16-byte loads per lane).
+//    flight while sub-block i is consumed (16 x 16-byte loads per lane).  The cache is read once,
+//    so its loads are nontemporal (streaming) and do not displace reusable lines in the caches.
 //  * Scores S^T = K q^T on v_mfma_f32_16x16x32_bf16: K goes from HBM straight into the A
 //    operand; the G query rows (padded to 16) form the B operand.  The rotated, scaled query is
 //    split into bf16 hi + lo parts and multiplied twice, so q keeps ~16 significant bits and K is
@@ -142,14 +143,14 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
       const bool ok = key < kend;
       const uint16_t* kp = kg + (int64_t)(ok ? key : kbeg) * D + 8 * g16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kst[kb][ks] = *reinterpret_cast<const u32x4*>(kp + 32 * ks);
+      for (int ks = 0; ks < KS; ++ks) kst[kb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * ks));
     }
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
       const int c = lane + 64 * i;
       const int key = k0 + c / NCH;
       const bool ok = key < kend;
-      vst[i] = *reinterpret_cast<const u32x4*>(vg + (int64_t)(ok ? key : kbeg) * D + (c % NCH) * 8);
+      vst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + (int64_t)(ok ? key : kbeg) * D + (c % NCH) * 8));
       if (!ok) vst[i] = u32x4{0, 0, 0, 0};
     }
   };

@@ -51,6 +51,11 @@ class Workload:
         """Causal half of the two S x S x D contractions: 2*B*Hq*S^2*D."""
         return 2.0 * self.B * self.Hq * self.S * self.S * self.D
 
+    def prefill_bytes(self) -> int:
+        """Bytes a prefill must move at least: read Q, K and V once, write O once."""
+        esz = 2 if self.dtype == "bf16" else 4
+        return (2 * self.B * self.Hq + 2 * self.B * self.Hkv) * self.S * self.D * esz
+
     def decode_kv_bytes(self) -> int:
         """K and V cache bytes one decode step must read."""
         esz = 2 if self.dtype == "bf16" else 4
