@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from conftest import assert_bf16_parity, assert_f32_parity, banner, err_stats, to_np
+from conftest import BF16_MAX_ABS, BF16_MEAN_ABS, assert_bf16_parity, assert_f32_parity, banner, err_stats, to_np
 from transformer_self_attention_amd import inputs
 
 pytestmark = pytest.mark.gpu
@@ -178,8 +178,10 @@ def test_prefill_gqa_config(lib):
 def test_prefill_long_config(lib):
     """Long workload at full size: S=32768, 1% of keys x8; 128 seeded rows per head.
 
-    Checked with fp32 output: rounding the exact result to bf16 storage alone costs a mean abs
-    error of ~8.6e-4 on this workload, so the bf16-output run is held to the max-abs bar."""
+    Checked with fp32 output against both bars.  Rounding the exact result to bf16 storage alone
+    costs a mean abs error of ~8.6e-4 on this workload (the rows dominated by a x8 key have |o|
+    near |v|), so the bf16-output run is held to the max-abs bar against the exact result and to
+    the mean-abs bar against the exact result rounded once to bf16 (same storage precision)."""
     wl = inputs.WORKLOADS["long"]
     banner("prefill long Hq=32 Hkv=8 S=32768 x8 keys (full config, 128 rows/head)")
     p = inputs.make_prefill(wl)
@@ -191,7 +193,11 @@ def test_prefill_long_config(lib):
     ob, _ = run_prefill(lib, p, out_dtype=torch.bfloat16)
     mx, mean = err_stats(take_rows(to_np(ob), p.rows), ref)
     print(f"    long o (bf16 out) max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
-    assert mx <= 2e-2
+    assert mx <= BF16_MAX_ABS
+    ref_b = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(ref.astype(np.float32)))
+    mx_b, mean_b = err_stats(take_rows(to_np(ob), p.rows), ref_b)
+    print(f"    long o (bf16 out) vs bf16-rounded exact: max_abs={mx_b:.3e} mean_abs={mean_b:.3e}", flush=True)
+    assert mean_b <= BF16_MEAN_ABS
 
 
 def test_two_stage_prefill_equals_one_call(lib):
