@@ -38,14 +38,13 @@ namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = kWaves * 64;
+constexpr int kWavesStream = 4;            // waves per workgroup
 constexpr int kRowsPerWave = 32;
-constexpr int kRowBlocks = 1;               // 32-row blocks per wave on the streaming paths
 constexpr int kBN = 64;                     // keys per tile
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kNumXcd = 8;
 constexpr int kWaitVmcnt0 = 0x0F70;          // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
+constexpr bool kOffsetInit = true;          // scores come out of the MFMA already offset by -m
 
 enum { KMODE_PREROT = 0, KMODE_FUSED = 1, KMODE_RAW = 2 };
 
@@ -59,21 +58,23 @@ __device__ __forceinline__ int swz(int r, int lc) {
   }
 }
 
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int RB>
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads), amdgpu_waves_per_eu(3 - RB, 3 - RB)))
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW>
+__global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 2, NW / 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int S, int pos0,
                          const float2* __restrict__ table) {
+  constexpr int NT = NW * 64;                // threads per workgroup
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over D
   constexpr int DB = D / 32;                 // 32-wide output blocks over D
   constexpr int TILE_ELEMS = kBN * D;
-  constexpr int DIRECT_PER_WAVE = TILE_ELEMS * 2 / 1024 / kWaves;  // 1 KB wave-loads per tensor
-  constexpr int CPT = kBN * NCH / kThreads;  // K chunks per thread (fused mode)
+  constexpr int DIRECT_PER_WAVE = TILE_ELEMS * 2 / 1024 / NW;  // 1 KB wave-loads per tensor
+  constexpr int CPT = kBN * NCH / NT;        // K chunks per thread (fused mode)
   constexpr bool QK_BF16 = KMODE == KMODE_RAW;
-  constexpr int ROWS = kRowsPerWave * RB;    // query rows per wave
-  constexpr int BM = kWaves * ROWS;          // query rows per workgroup
+  constexpr int BM = NW * kRowsPerWave;      // query rows per workgroup
+  static_assert(DIRECT_PER_WAVE * 1024 * NW == TILE_ELEMS * 2, "tile split over waves");
+  static_assert(CPT * NT == kBN * NCH, "fused tile split over threads");
 
   // Two stages, as four distinct LDS objects: with the stage fixed at compile time (the key loop
   // is unrolled by two) the compiler can see that the HBM->LDS loads of the next tile never
@@ -107,26 +108,23 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int g16 = lane >> 4;     // 16-lane group
   const int i16 = lane & 15;
   const int q0 = qblock * BM;
-  const int qw = q0 + wave * ROWS;          // first row of this wave
-  int row[RB];                              // this lane's query row in each row block
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) row[rb] = qw + 32 * rb + l32;
+  const int qw = q0 + wave * kRowsPerWave;  // first row of this wave
+  const int row = qw + l32;                 // this lane's query row
   // exp2 argument scale: folded into Q (fp16 modes) or applied to raw scores (bf16 mode)
   const float c_log2 = 1.4426950408889634f / sqrtf((float)D);
 
   // ---- Q fragments (B operand) ----
   typedef typename std::conditional<QK_BF16, bf16x8, f16x8>::type qk_t;
-  qk_t qf[RB][KS];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const int rc = row[rb] < S ? row[rb] : S - 1;
+  qk_t qf[KS];
+  {
+    const int rc = row < S ? row : S - 1;
     const uint16_t* qrow = q + (((int64_t)b * Hq + h) * S + rc) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * hl;
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
       if constexpr (QK_BF16) {
-        qf[rb][ks] = __builtin_bit_cast(bf16x8, w);
+        qf[ks] = __builtin_bit_cast(bf16x8, w);
       } else {
         float x[8];
 #pragma unroll
@@ -142,7 +140,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p + 1] = x0 * s + x1 * c;
         }
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qf[rb][ks][t] = (_Float16)(x[t] * c_log2);
+        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
       }
     }
   }
@@ -155,7 +153,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const uint16_t* kg = k + kv_off;
   const uint16_t* vg = v + kv_off;
   // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
-  // [(i * kWaves + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
+  // [(i * NW + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
   // of row P / NCH.  The per-lane element offsets are fixed for the whole kernel; each tile adds
   // a wave-uniform base.  Rows past S read row S-1 (finite data; those keys are masked).
   // Byte offsets are unsigned 32-bit so the loads use the scalar-base + vector-offset form.
@@ -163,7 +161,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   int dma_row[DIRECT_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
-    const int P = (i * kWaves + wave) * 64 + lane;
+    const int P = (i * NW + wave) * 64 + lane;
     const int r = P / NCH;
     dma_row[i] = r;
     dma_byte[i] = (uint32_t)(r * D + swz<D>(r, P % NCH) * 8) * 2u;
@@ -177,7 +175,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
         const uint32_t off = dma_byte[i];
         const void* g = base + off;
-        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * kWaves + wave) * 512);
+        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
         __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
       }
     } else {
@@ -187,7 +185,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         const int rr = min(r, S - 1 - k0);
         const uint32_t off = dma_byte[i] - (uint32_t)((r - rr) * D * 2);
         const void* g = base + off;
-        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * kWaves + wave) * 512);
+        ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
         __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
       }
     }
@@ -216,7 +214,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if constexpr (KMODE == KMODE_FUSED) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NT * i;
         const int r = c / NCH, cc = c % NCH;
         const int key = min(k0 + r, S - 1);
         kst[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * D + cc * 8);
@@ -230,7 +228,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if constexpr (KMODE == KMODE_FUSED) {
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
-        const int c = tid + kThreads * i;
+        const int c = tid + NT * i;
         const int r = c / NCH, cc = c % NCH;
         float x[8];
 #pragma unroll
@@ -258,20 +256,19 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   };
 
   // ---- accumulators ----
-  f32x16 oacc[RB][DB];
+  f32x16 oacc[DB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int db = 0; db < DB; ++db)
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
+  float m_run = -INFINITY;  // running row max of the exp2-domain scores
+  float l_run = 0.f;        // this lane's half of the row sum
+  // Offset the score MFMA starts from: -m_run once m_run is finite (the scores then come out as
+  // s - m_run and need no subtraction); 0 before the first tile.
+  float s_init = 0.f;
+  f32x16 s_init_v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[rb][db][r] = 0.f;
-  float m_run[RB];   // running row max of the exp2-domain scores
-  float l_run[RB];   // this lane's half of the row sum
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    m_run[rb] = -INFINITY;
-    l_run[rb] = 0.f;
-  }
+  for (int r = 0; r < 16; ++r) s_init_v[r] = 0.f;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
@@ -291,11 +288,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
 
-    if (!CAUSAL || k0 <= qw + ROWS - 1) {
+    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
       const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
-      // S^T = K Q^T for two 32-key blocks; each K fragment feeds every row block
-      f32x16 sacc[RB][2];
+      // S^T = K Q^T for two 32-key blocks
+      f32x16 sacc[2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         qk_t a[KS];
@@ -303,60 +300,62 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         for (int ks = 0; ks < KS; ++ks)
           a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>((const ATTN_LDS char*)kb_lds + kaddr[ks] + kb * 32 * D * 2);
 #pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
+        for (int ks = 0; ks < KS; ++ks) {
+          // the first product starts from the offset block (s_init in every element)
+          const f32x16 c = ks == 0 ? s_init_v : sacc[kb];
+          if constexpr (QK_BF16)
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], c, 0, 0, 0);
+          else
+            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], c, 0, 0, 0);
+        }
+      }
+      if constexpr (QK_BF16) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sacc[rb][kb][r] = 0.f;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
+          for (int r = 0; r < 16; ++r) sacc[kb][r] *= c_log2;
+      }
+      // mask (diagonal / tail tiles only)
+      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw) || (k0 + kBN > S);
+      if (need_mask) {
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb) {
-            if constexpr (QK_BF16)
-              sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[rb][ks], sacc[rb][kb], 0, 0, 0);
-            else
-              sacc[rb][kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[rb][ks], sacc[rb][kb], 0, 0, 0);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            if ((CAUSAL && key > row) || key >= S) sacc[kb][r] = -INFINITY;
           }
       }
-      bf16x8 pf[RB][2][2];
+      // row max over this tile (relative to the offset the scores start from)
+      float mx = sacc[0][0];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        if constexpr (QK_BF16) {
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sacc[rb][kb][r] *= c_log2;
-        }
-        // mask (diagonal / tail tiles only)
-        const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw + 32 * rb) || (k0 + kBN > S);
-        if (need_mask) {
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-              if ((CAUSAL && key > row[rb]) || key >= S) sacc[rb][kb][r] = -INFINITY;
-            }
-        }
-        // row max over this tile
-        float mx = sacc[rb][0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[rb][0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[rb][1][r]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run[rb], mx);
-        const bool need = m_new > m_run[rb] + kRescaleThreshold;
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      bf16x8 pf[2][2];
+      float lsum = 0.f;
+      if constexpr (kOffsetInit && !QK_BF16) {
+        // sacc = s - m_run (s itself while m_run is -inf); mx is the tile max on that scale
+        const bool need = (m_run == -INFINITY) || (mx > kRescaleThreshold);
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float alpha = fast_exp2(m_run[rb] - m_new);
-          l_run[rb] *= alpha;
+          const float m_new = m_run == -INFINITY ? mx : m_run + fmaxf(mx, 0.f);
+          const float alpha = fast_exp2(m_run - m_new);   // 0 while m_run is -inf
+          const float shift = m_new + s_init;             // subtract to put sacc on m_new's scale
+          l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) oacc[rb][db][r] *= alpha;
-          m_run[rb] = m_new;
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
+          m_run = m_new;
+          s_init = -m_new;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s_init_v[r] = s_init;
         }
-        // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
-        // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
-        float lsum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -364,15 +363,42 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
             for (int tt = 0; tt < 8; tt += 2) {
               bf16x2 pp;
-              pp[0] = (__bf16)fast_exp2(sacc[rb][kb][8 * s + tt] - m_run[rb]);
-              pp[1] = (__bf16)fast_exp2(sacc[rb][kb][8 * s + tt + 1] - m_run[rb]);
-              pf[rb][kb][s][tt] = pp[0];
-              pf[rb][kb][s][tt + 1] = pp[1];
+              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt]);
+              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1]);
+              pf[kb][s][tt] = pp[0];
+              pf[kb][s][tt + 1] = pp[1];
               lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
             }
-        l_run[rb] += lsum;
+      } else {
+        const float m_new = fmaxf(m_run, mx);
+        const bool need = m_new > m_run + kRescaleThreshold;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+          const float alpha = fast_exp2(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+          m_run = m_new;
+        }
+        // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
+        // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tt = 0; tt < 8; tt += 2) {
+              bf16x2 pp;
+              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt] - m_run);
+              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1] - m_run);
+              pf[kb][s][tt] = pp[0];
+              pf[kb][s][tt + 1] = pp[1];
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+            }
       }
-      // O^T += V^T P^T; each V^T fragment feeds every row block
+      l_run += lsum;
+      // O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         bf16x8 va[2][DB];
@@ -394,9 +420,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int db = 0; db < DB; ++db)
-#pragma unroll
-            for (int rb = 0; rb < RB; ++rb)
-              oacc[rb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[rb][kb][s], oacc[rb][db], 0, 0, 0);
+            oacc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s][db], pf[kb][s], oacc[db], 0, 0, 0);
       }
     }
     // Fused RoPE: the next tile's keys and coefficients are fetched only now, so the staging
@@ -413,31 +437,27 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 
   // ---- finalize ----
+  const float l_tot = l_run + swap_halves(l_run);
+  if (row < S) {
+    const float inv = 1.0f / l_tot;
+    const int64_t orow = (((int64_t)b * Hq + h) * S + row) * D;
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const float l_tot = l_run[rb] + swap_halves(l_run[rb]);
-    if (row[rb] < S) {
-      const float inv = 1.0f / l_tot;
-      const int64_t orow = (((int64_t)b * Hq + h) * S + row[rb]) * D;
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int d0 = db * 32 + 8 * r4 + 4 * hl;
-          const float o0 = oacc[rb][db][4 * r4 + 0] * inv, o1 = oacc[rb][db][4 * r4 + 1] * inv;
-          const float o2 = oacc[rb][db][4 * r4 + 2] * inv, o3 = oacc[rb][db][4 * r4 + 3] * inv;
-          if constexpr (OUT_BF16) {
-            u32x2 w;
-            w[0] = pack_bf16(o0, o1);
-            w[1] = pack_bf16(o2, o3);
-            *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o) + orow + d0) = w;
-          } else {
-            *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
-          }
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = db * 32 + 8 * r4 + 4 * hl;
+        const float o0 = oacc[db][4 * r4 + 0] * inv, o1 = oacc[db][4 * r4 + 1] * inv;
+        const float o2 = oacc[db][4 * r4 + 2] * inv, o3 = oacc[db][4 * r4 + 3] * inv;
+        if constexpr (OUT_BF16) {
+          u32x2 w;
+          w[0] = pack_bf16(o0, o1);
+          w[1] = pack_bf16(o2, o3);
+          *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(o) + orow + d0) = w;
+        } else {
+          *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
         }
-      if (lse && hl == 0)
-        lse[((int64_t)b * Hq + h) * S + row[rb]] = (m_run[rb] + log2f(l_tot)) * 0.6931471805599453f;
-    }
+      }
+    if (lse && hl == 0) lse[((int64_t)b * Hq + h) * S + row] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
@@ -469,21 +489,16 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
   }
 }
 
-// Row blocks per wave: two (64 query rows per wave, one wave per SIMD) on the streaming paths,
-// one for the fused-RoPE path, whose staged key registers would not fit beside two blocks.
-template <int KMODE>
-constexpr int row_blocks() { return KMODE == KMODE_FUSED ? 1 : kRowBlocks; }
-
 template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
 hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
-  constexpr int RB = row_blocks<KMODE>();
-  constexpr int BM = kWaves * kRowsPerWave * RB;
+  constexpr int NW = kWavesStream;
+  constexpr int BM = NW * kRowsPerWave;
   const int G = a.Hq / a.Hkv;
   const int nqb = (a.S + BM - 1) / BM;
   const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, RB>), dim3((unsigned)blocks),
-                     dim3(kThreads), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW>), dim3((unsigned)blocks),
+                     dim3(NW * 64), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.pos0,
                      reinterpret_cast<const float2*>(a.table));
   return hipGetLastError();
