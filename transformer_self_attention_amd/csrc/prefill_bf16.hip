@@ -44,6 +44,7 @@ constexpr int kBN = 64;                     // keys per tile
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kNumXcd = 8;
 constexpr int kWaitVmcnt0 = 0x0F70;          // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
+constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3: 32-bit data format, raw
 constexpr bool kOffsetInit = true;          // scores come out of the MFMA already offset by -m
 
 enum { KMODE_PREROT = 0, KMODE_FUSED = 1, KMODE_RAW = 2 };
@@ -171,12 +172,15 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // elements inside the builtin's argument list and would silently drop the kernel)
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * D);
     if (k0 + kBN <= S) {
+      // full tile: a buffer resource over the tile (scalar work only) and the fixed per-lane
+      // offsets, so no per-lane address arithmetic is repeated per tile
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, kBN * D * 2, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
         const uint32_t off = dma_byte[i];
-        const void* g = base + off;
         ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
-        __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, l, 16, (int)off, 0, 0, 0);
       }
     } else {
 #pragma unroll
