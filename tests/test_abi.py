@@ -148,7 +148,8 @@ def test_prefill_workspace_bytes():
 def test_decode_workspace_geometry():
     B, Hq, Hkv, S, D = 32, 64, 8, 8192, 128
     ns = lib.decode_num_splits(B, Hq, Hkv, S, D, 0)
-    assert ns == 2                     # 256 (sequence, KV head) units x 2 splits = 512 workgroups
+    assert ns == 1                     # 256 (sequence, KV head) units: one workgroup each, no merge
+    assert lib.decode_num_splits(8, 64, 8, 8192, 128, 0) == 8   # 64 units x 8 splits = 512 workgroups
     assert lib.decode_workspace_bytes(B, Hq, Hkv, S, D, 0) == B * Hq * ns * (D + 2) * 4
     # explicit split counts are honoured up to whole 32-key chunks
     assert lib.decode_num_splits(1, 8, 1, 200, 64, 3) == 3   # 67 keys -> 96-key chunks

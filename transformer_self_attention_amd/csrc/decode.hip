@@ -1,5 +1,5 @@
-// Decode: one new query per sequence against a KV cache, split over the cache ("split-K"),
-// followed by a merge pass.
+// Decode: one new query per sequence against a KV cache, optionally split over the cache
+// ("split-K") with a merge pass.
 //
 // Method: the KV-cache decode step of ninaddeshpande.com "Transformer internals: attention
 // without the mysticism" ("The KV cache and the memory wall"): each query row attends to every
@@ -7,8 +7,8 @@
 // (devthesis.com section 3) at its own position.  The G = Hq/Hkv query heads that share a KV head
 // (codingpancake.com section 6.1) are processed together so each K/V byte is read once.
 //
-// Pass 1 (decode_split_kernel), one workgroup per (sequence, KV head, split):
-//  * 4 waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
+// decode_split_kernel, one workgroup per (sequence, KV head, split):
+//  * The waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
 //    flight while sub-block i is consumed (16 x 16-byte loads per lane).  The cache is read once,
 //    so its loads are nontemporal (streaming) and do not displace reusable lines in the caches.
 //  * Scores S^T = K q^T on v_mfma_f32_16x16x32_bf16: K goes from HBM straight into the A
@@ -19,17 +19,19 @@
 //    lazy rescaling as in prefill.
 //  * O^T += V^T P^T on the same MFMA shape; V^T comes from a wave-private LDS tile through
 //    ds_read_b64_tr_b16.
-//  * The 4 waves' (m, l, O) are merged through LDS and one partial per (row, split) is written.
-// Pass 2 (decode_merge_kernel), one workgroup per (sequence, query head): combines the splits
-// with the same log-sum-exp algebra and writes o and lse.
+//  * The waves' (m, l, O) are merged through LDS.  With one split (8 waves per workgroup, used
+//    when there are enough (sequence, KV head) pairs to fill the GPU) the workgroup writes o and
+//    lse directly; otherwise (4 waves per workgroup) it writes one partial per (row, split).
+// decode_merge_kernel, one workgroup per (sequence, query head), only after a split cache:
+// combines the splits with the same log-sum-exp algebra and writes o and lse.
 #include "common.h"
 
 namespace attn {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kWavesSplit = 4;   // waves per workgroup when the cache is split (merge pass after)
+constexpr int kWavesWhole = 8;   // waves per workgroup when one workgroup covers the whole cache
 constexpr int kSub = 32;   // keys per wave iteration
 constexpr float kRescaleThreshold = 8.0f;
 
@@ -55,12 +57,17 @@ __device__ __forceinline__ int vswz(int r, int lc) {  // 16 chunks per row (D = 
   return lc ^ (((r & 3) << 2) | ((r >> 2) & 3));
 }
 
-template <int D, bool ROPE>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(
+// NW waves per workgroup.  WHOLE: one split covers the whole cache, and the workgroup writes the
+// final o (OUT_BF16 selects its type) and lse itself; otherwise it writes one partial (m, l, O)
+// per (row, split) for decode_merge_kernel.
+template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16>
+__global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int Hq, int Hkv,
     int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml) {
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse) {
+  constexpr int kWaves = NW;
+  constexpr int kThreads = NW * 64;
   constexpr int NCH = D / 8;
   constexpr int KS = D / 32;        // MFMA k-steps over D
   constexpr int DB = D / 16;        // 16-wide output blocks over D
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
     int pos = 0;
     if constexpr (ROPE) {
       pos = q_pos[b];
-      if (pos < 0 || pos >= table_max_pos) pos = 0;  // the merge pass reports such rows as NaN
+      if (pos < 0 || pos >= table_max_pos) pos = 0;  // such rows are written as NaN at the end
     }
     const bool valid = qrow < G;
     const uint16_t* qp = q + ((int64_t)b * Hq + hkv * G + (valid ? qrow : 0)) * D;
@@ -260,11 +267,27 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(
         acc += red_o[(w * 16 + rr) * D + d] * sc;
       }
     }
-    const int64_t part = (((int64_t)b * Hq + hkv * G + rr) * n_split + split);
-    ws_o[part * D + d] = acc;
-    if (d == 0) {
-      ws_ml[part * 2 + 0] = M;
-      ws_ml[part * 2 + 1] = Lsum;
+    if constexpr (WHOLE) {
+      float out = Lsum > 0.f ? acc / Lsum : 0.f;
+      float ls = Lsum > 0.f ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
+      if constexpr (ROPE) {
+        const int p = q_pos[b];
+        if (p < 0 || p >= table_max_pos) { out = __builtin_nanf(""); ls = __builtin_nanf(""); }
+      }
+      const int64_t oi = ((int64_t)b * Hq + hkv * G + rr) * D + d;
+      if constexpr (OUT_BF16) {
+        reinterpret_cast<__bf16*>(o)[oi] = (__bf16)out;
+      } else {
+        reinterpret_cast<float*>(o)[oi] = out;
+      }
+      if (lse && d == 0) lse[(int64_t)b * Hq + hkv * G + rr] = ls;
+    } else {
+      const int64_t part = (((int64_t)b * Hq + hkv * G + rr) * n_split + split);
+      ws_o[part * D + d] = acc;
+      if (d == 0) {
+        ws_ml[part * 2 + 0] = M;
+        ws_ml[part * 2 + 1] = Lsum;
+      }
     }
   }
 }
@@ -302,10 +325,25 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
 
 template <int D, bool ROPE>
 hipError_t go(const DecodeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL((decode_split_kernel<D, ROPE>), dim3(a.n_split, a.Hkv, a.B), dim3(kThreads), 0, st,
-                     (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v, a.cache_len,
-                     a.q_pos, a.Hq, a.Hkv, a.S_max, reinterpret_cast<const float2*>(a.table),
-                     a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml);
+  const uint16_t* q = (const uint16_t*)a.q;
+  const uint16_t* kc = (const uint16_t*)a.k;
+  const uint16_t* vc = (const uint16_t*)a.v;
+  const float2* tab = reinterpret_cast<const float2*>(a.table);
+  if (a.n_split == 1) {
+    // one workgroup per (sequence, KV head) streams the whole cache and writes o itself
+    if (a.out_bf16)
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true>), dim3(1, a.Hkv, a.B),
+                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
+                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
+    else
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false>), dim3(1, a.Hkv, a.B),
+                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
+                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false>), dim3(a.n_split, a.Hkv, a.B),
+                     dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max, tab,
+                     a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.out_bf16)
