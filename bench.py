@@ -9,7 +9,8 @@ One step = one pass of the hot path over the workload's synthetic batch:
     can bracket the attention kernel inside the timed region; attn_prefill enqueues exactly the
     same two kernels (a GPU test checks that both routes give identical bytes).
   * decode (sub-object ``decode``): batch 32 against an 8192-token cache, Hq=64, Hkv=8, D=128,
-    query rotated at position 8192; one attn_decode call (split + merge launches).
+    query rotated at position 8192; one attn_decode call (for this shape one launch: a workgroup
+    per (sequence, KV head) streams the whole cache).
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
     key rows scaled by 8.
 
@@ -47,11 +48,11 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 159360.2 KiB, WRITE_SIZE 131072.1 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 460587520, "sources_sha256_16": "0323c28bb296fea3"},
-    # decode_split_kernel + decode_merge_kernel, B=32 L=8192 Hq=64 Hkv=8 D=128, n_split 2 (4 each):
-    # FETCH_SIZE 525265.1 + 1159.5 KiB, WRITE_SIZE 2112.0 + 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1080804557, "sources_sha256_16": "c345e9745862076f"},
+    # FETCH_SIZE 158358.8 KiB, WRITE_SIZE 131089.8 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 458554778, "sources_sha256_16": "4e5d1a5c94014579"},
+    # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (4 dispatches):
+    # FETCH_SIZE 524919.5 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1075559424, "sources_sha256_16": "5102dbf7223a748a"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
@@ -310,7 +311,9 @@ def main():
                "config": {"workload": "batch decode against a KV cache", "B": wl.B, "cache_len": wl.S,
                           "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D, "n_split": r["n_split"],
                           "kv_bytes_per_step": wl.decode_kv_bytes()},
-               "roofline": {"bound": "hbm", "kernel": "decode_split_kernel + decode_merge_kernel",
+               "roofline": {"bound": "hbm",
+                            "kernel": ("decode_split_kernel (whole cache per workgroup, writes o)"
+                                       if r["n_split"] == 1 else "decode_split_kernel + decode_merge_kernel"),
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                             "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode")}}
         if "prefill" not in res:
