@@ -179,14 +179,15 @@ def bench_decode(lib, inputs, wl, steps, warmup):
                      device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] timing decode: warmup {warmup}, steps {steps}")
-    # One step is one attn_decode call (its split and merge launches back to back); the steps are
-    # timed as a whole, without events between them.
+    # One step is one attn_decode call; the steps are timed as a whole, without events between
+    # them.  A decode step is ~0.16 ms, so it runs 4x the prefill step count (the clock settles
+    # after the idle gap at the synchronize that opens the timed region).
     ms = time_calls(lambda: lib.decode(q, kc, vc, cl, qp, tab, out=out, workspace=ws), steps, warmup)
     nbytes = wl.decode_kv_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
     n_split = lib.decode_num_splits(wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, 0)
-    return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split}
+    return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
 
 
 def cpu_threads():
@@ -268,7 +269,7 @@ def main():
     if args.only in ("prefill", "all"):
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
     if args.only in ("decode", "all"):
-        res["decode"] = bench_decode(lib, inputs, W["decode"], args.steps, args.warmup)
+        res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only == "long" or (args.only == "all" and not args.no_long):
         res["long"] = bench_prefill(lib, inputs, W["long"], max(3, args.steps // 5), max(2, args.warmup // 5),
                                     variants=False)
@@ -307,7 +308,7 @@ def main():
         wl = r["d"].wl
         gbs = r["gbs"]
         dec = {"metric": "decode KV-read GB/s", "value": round(gbs, 1), "unit": "GB/s",
-               "ms_per_step": round(r["ms"], 5),
+               "ms_per_step": round(r["ms"], 5), "steps": r["steps"], "warmup": r["warmup"],
                "config": {"workload": "batch decode against a KV cache", "B": wl.B, "cache_len": wl.S,
                           "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D, "n_split": r["n_split"],
                           "kv_bytes_per_step": wl.decode_kv_bytes()},
