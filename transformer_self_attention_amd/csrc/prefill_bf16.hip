@@ -42,6 +42,7 @@ constexpr int kWavesStream = 4;            // waves per workgroup
 constexpr int kRowsPerWave = 32;
 constexpr int kBN = 64;                     // keys per tile
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+constexpr float kWeightSumBound = 1024.0f;  // per-lane weight sum that forces a max update
 constexpr int kNumXcd = 8;
 constexpr int kWaitVmcnt0 = 0x0F70;          // s_waitcnt vmcnt(0) expcnt(7) lgkmcnt(15)
 constexpr int kBufferWord3 = 0x00020000;     // buffer resource word 3: 32-bit data format, raw
@@ -330,19 +331,43 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
             if ((CAUSAL && key > row) || key >= S) sacc[kb][r] = -INFINITY;
           }
       }
-      // row max over this tile (relative to the offset the scores start from)
-      float mx = sacc[0][0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
-      mx = fmaxf(mx, swap_halves(mx));
       bf16x8 pf[2][2];
       float lsum = 0.f;
+      // p = 2^score rounded to bf16 (the B operand of P.V); the row sum adds the same rounded
+      // weights, two at a time (v_dot2_f32_bf16 against (1, 1))
+      auto weights = [&]() __attribute__((always_inline)) {
+        lsum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int tt = 0; tt < 8; tt += 2) {
+              bf16x2 pp;
+              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt]);
+              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1]);
+              pf[kb][s][tt] = pp[0];
+              pf[kb][s][tt + 1] = pp[1];
+              lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+            }
+      };
+      auto tile_max = [&]() __attribute__((always_inline)) {
+        float mx = sacc[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, sacc[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[1][r]);
+        return fmaxf(mx, swap_halves(mx));
+      };
       if constexpr (kOffsetInit && !QK_BF16) {
-        // sacc = s - m_run (s itself while m_run is -inf); mx is the tile max on that scale
-        const bool need = (m_run == -INFINITY) || (mx > kRescaleThreshold);
-        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        // sacc = s - m_run (s itself while m_run is -inf).  The weights are formed directly; the
+        // tile max is taken only when this lane's weight sum leaves [0, kWeightSumBound] (some
+        // score rose well above m_run; the first tile, where m_run is -inf, always does).  Then O
+        // and l move to the tile max and the weights are formed again.  Without that, every
+        // weight is at most kWeightSumBound, so O and l stay far from overflow.
+        weights();
+        if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY || !(lsum <= kWeightSumBound)) != 0) {
+          const float mx = tile_max();
           const float m_new = m_run == -INFINITY ? mx : m_run + fmaxf(mx, 0.f);
           const float alpha = fast_exp2(m_run - m_new);   // 0 while m_run is -inf
           const float shift = m_new + s_init;             // subtract to put sacc on m_new's scale
@@ -359,21 +384,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           s_init = -m_new;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_init_v[r] = s_init;
+          weights();
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int tt = 0; tt < 8; tt += 2) {
-              bf16x2 pp;
-              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt]);
-              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1]);
-              pf[kb][s][tt] = pp[0];
-              pf[kb][s][tt + 1] = pp[1];
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
-            }
       } else {
+        const float mx = tile_max();
         const float m_new = fmaxf(m_run, mx);
         const bool need = m_new > m_run + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
