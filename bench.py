@@ -11,6 +11,7 @@ One step = one pass of the hot path over the workload's synthetic batch:
   * decode (sub-object ``decode``): batch 32 against an 8192-token cache, Hq=64, Hkv=8, D=128,
     query rotated at position 8192; one attn_decode call (for this shape one launch: a workgroup
     per (sequence, KV head) streams the whole cache).
+  * MHA (sub-object ``mha_prefill``): B=4, H=32, S=2048, D=128 prefill, same step.
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
     key rows scaled by 8.
 
@@ -270,6 +271,8 @@ def main():
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
+    if args.only == "all":
+        res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False)
     if args.only == "long" or (args.only == "all" and not args.no_long):
         res["long"] = bench_prefill(lib, inputs, W["long"], max(3, args.steps // 5), max(2, args.warmup // 5),
                                     variants=False)
@@ -321,6 +324,14 @@ def main():
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"],
                         "config": dec["config"], "roofline": dec["roofline"]})
         out["decode"] = dec
+    if "mha" in res:
+        r = res["mha"]
+        wl = r["p"].wl
+        out["mha_prefill"] = {
+            "value": round(r["tflops_step"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_step"], 5),
+            "frac": round(r["tflops_step"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attention_kernel_tflops": round(r["tflops_kernel"], 2),
+            "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D}}
     if "long" in res:
         r = res["long"]
         wl = r["p"].wl
