@@ -49,11 +49,11 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 158358.8 KiB, WRITE_SIZE 131089.8 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 458554778, "sources_sha256_16": "4e5d1a5c94014579"},
-    # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (4 dispatches):
-    # FETCH_SIZE 524919.5 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1075559424, "sources_sha256_16": "5102dbf7223a748a"},
+    # FETCH_SIZE 158333.0 KiB, WRITE_SIZE 131086.6 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 458498662, "sources_sha256_16": "d29708186043597d"},
+    # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
+    # FETCH_SIZE 524914.4 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1075548979, "sources_sha256_16": "5102dbf7223a748a"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
