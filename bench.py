@@ -50,10 +50,10 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
     # FETCH_SIZE 158333.0 KiB, WRITE_SIZE 131086.6 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 458498662, "sources_sha256_16": "d29708186043597d"},
+    "prefill_gqa": {"bytes_per_launch": 458498662, "sources_sha256_16": "cb0f9f15ae093d17"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
     # FETCH_SIZE 524914.4 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1075548979, "sources_sha256_16": "5102dbf7223a748a"},
+    "decode": {"bytes_per_launch": 1075548979, "sources_sha256_16": "98838bc4dfe63493"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",

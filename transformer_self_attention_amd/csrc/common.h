@@ -52,11 +52,6 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // A value known to be the same in every lane, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
-// Empty asm that uses a value: the value must be computed before this point in program order.
-// Keeps the optimiser from sinking arithmetic out of the code region it was scheduled into.
-__device__ __forceinline__ void pin_value(bf16x8 x) { asm volatile("" ::"v"(x)); }
-__device__ __forceinline__ void pin_value(float x) { asm volatile("" ::"v"(x)); }
-
 // ------------------------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() of its launch).  Arguments were validated by the
 // C-ABI layer; the launchers only size grids.
