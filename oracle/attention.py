@@ -26,11 +26,18 @@ What it computes is the plain definition, written out with NumPy in float64:
   (ninaddeshpande.com), "The KV cache and the memory wall": one new query per sequence
   attends to every cached key.  The cache is used as stored (already rotated); the
   query is rotated at its own position.
+* Chunked prefill against a cache -- the same page and section (keys and values of
+  earlier tokens are kept and reused), with the chunked prefill named on "Multi-Head
+  Attention & Rotary Position Embeddings (RoPE)" (learnllm.online), "Prefill vs Decode
+  Latency & Memory Wall Waterfall": a chunk of Sq new tokens at positions pos0 .. pos0+Sq-1
+  first appends its rotated keys (stored in bfloat16, the cache's format) and its values to
+  the cache, then each new query attends to every cache row up to and including its own
+  position (the causal mask aligned at the bottom right of the Sq x (pos0+Sq) score block).
 
 Every score row is materialised in full (no tiling over keys, no running max/sum), so
 nothing here mirrors the GPU's online-softmax recurrence.
 
-Pins (tests/test_oracle.py): the pages' Problem 1 and Problem 2 numbers, RoPE norm
+Pins (tests/test_oracle.py, tests/test_oracle_cache.py): the pages' Problem 1 and Problem 2 numbers, RoPE norm
 preservation, the Problem 3 closed form of the rotated inner product, relative-position
 invariance, identity at position 0, softmax rows summing to one, causal row 0 == V[0],
 zero-Q prefix means, permutation equivariance, torch's CPU
@@ -41,7 +48,8 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["rope_frequencies", "rope", "attention", "decode"]
+__all__ = ["rope_frequencies", "rope", "attention", "decode", "round_bf16", "append_to_cache",
+           "attention_with_cache"]
 
 
 def rope_frequencies(D: int, base: float = 10000.0) -> np.ndarray:
@@ -168,4 +176,82 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0):
             w, ls = _softmax_rows(s)
             o[b, kv * G:(kv + 1) * G, 0, :] = w @ vc[b, kv, :L]
             lse[b, kv * G:(kv + 1) * G] = ls
+    return o, lse
+
+
+def round_bf16(x) -> np.ndarray:
+    """Round to the nearest bfloat16 value (8 significant bits, ties to even); float64 result.
+
+    This is the storage format of the KV cache: keys rotated for a chunk are kept in it at this
+    precision.  Written from the format's definition: x = m * 2^e with 0.5 <= |m| < 1, so m * 2^8
+    is rounded to an integer (numpy rounds halves to even).  Zeros and non-finite values pass
+    through; the bfloat16 subnormal range (|x| < 2^-126) is not treated specially.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = x.copy()
+    nz = np.isfinite(x) & (x != 0.0)
+    m, e = np.frexp(x[nz])
+    out[nz] = np.ldexp(np.round(m * 256.0), e - 8)
+    return out
+
+
+def append_to_cache(k_cache, v_cache, k_new, v_new, pos0: int, *, rope_base=10000.0):
+    """Cache after a chunk of Sq new tokens is written into rows [pos0, pos0 + Sq).
+
+    k_cache, v_cache: [B, Hkv, S_max, D]; k_new, v_new: [B, Hkv, Sq, D].  Key row s is rotated
+    at position pos0 + s (unless rope_base is None) and stored rounded to bfloat16; values are
+    stored as given.  Rows outside [pos0, pos0 + Sq) are unchanged.  Returns new arrays.
+    """
+    kc = np.array(k_cache, dtype=np.float64, copy=True)
+    vc = np.array(v_cache, dtype=np.float64, copy=True)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    Sq = k_new.shape[2]
+    if pos0 < 0 or pos0 + Sq > kc.shape[2]:
+        raise ValueError("chunk does not fit the cache")
+    kr = rope(k_new, pos0 + np.arange(Sq), rope_base) if rope_base is not None else k_new
+    kc[:, :, pos0:pos0 + Sq] = round_bf16(kr)
+    vc[:, :, pos0:pos0 + Sq] = v_new
+    return kc, vc
+
+
+def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, rows=None):
+    """A chunk of Sq queries at positions pos0 .. pos0+Sq-1 against the cache rows [0, pos0 + Sq).
+
+    q: [B, Hq, Sq, D] (rotated here at pos0 + i unless rope_base is None); k_cache, v_cache:
+    [B, Hkv, S_max, D] used as stored (the chunk's own keys already appended).  Query i sees
+    key j only if j <= pos0 + i.  rows: None for every row, or an int array [Hq, n].
+    Returns (o [B, Hq, n, D], lse [B, Hq, n]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    kc = np.asarray(k_cache, dtype=np.float64)
+    vc = np.asarray(v_cache, dtype=np.float64)
+    B, Hq, Sq, D = q.shape
+    Hkv = kc.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    Sk = pos0 + Sq
+    if pos0 < 0 or Sk > kc.shape[2]:
+        raise ValueError("chunk does not fit the cache")
+    G = Hq // Hkv
+    if rows is None:
+        rows = np.broadcast_to(np.arange(Sq), (Hq, Sq))
+    rows = np.asarray(rows)
+    n = rows.shape[1]
+    keys = np.arange(Sk)
+    scale = 1.0 / np.sqrt(D)
+    o = np.empty((B, Hq, n, D))
+    lse = np.empty((B, Hq, n))
+    for b in range(B):
+        for h in range(Hq):
+            kv = h // G
+            r = rows[h]
+            qh = q[b, h, r]
+            if rope_base is not None:
+                qh = rope(qh, pos0 + r, rope_base)
+            s = (qh @ kc[b, kv, :Sk].T) * scale                  # [n, pos0 + Sq] full rows
+            s = np.where(keys[None, :] > pos0 + r[:, None], -np.inf, s)
+            w, ls = _softmax_rows(s)
+            o[b, h] = w @ vc[b, kv, :Sk]
+            lse[b, h] = ls
     return o, lse
