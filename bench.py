@@ -14,6 +14,10 @@ One step = one pass of the hot path over the workload's synthetic batch:
   * MHA (sub-object ``mha_prefill``): B=4, H=32, S=2048, D=128 prefill, same step.
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
     key rows scaled by 8.
+  * chunk (sub-object ``chunk_prefill``): the last 2048-token chunk of an 8192-token GQA prompt
+    (B=1, Hq=64, Hkv=8, D=128) against the 6144 tokens already in the KV cache; one
+    attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
+    chunk's queries against cache rows [0, 8192) with the bottom-right causal mask).
 
 Inputs are resident in HBM before timing starts.  W untimed warmup steps, then K timed steps
 bracketed by torch.cuda.synchronize(), timed with HIP events recorded on the stream the library
@@ -89,7 +93,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunk", "all"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -191,6 +195,27 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
 
 
+def bench_chunk(lib, inputs, wl, steps, warmup):
+    import torch
+    log(f"[bench] generating chunk inputs B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} Sq={wl.S} pos0={wl.pos0} "
+        f"S_max={wl.S_max} D={wl.D}")
+    c = inputs.make_chunk(wl)
+    q, kn, vn = c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda")
+    kc, vc = c.k_cache.torch("cuda"), c.v_cache.torch("cuda")
+    tab = lib.make_rope_table(wl.S_max, wl.D)
+    out = torch.empty_like(q)
+    ws = torch.empty(lib.prefill_workspace_bytes(wl.B, wl.Hkv, wl.pos0 + wl.S, wl.D), dtype=torch.uint8,
+                     device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] timing chunk prefill: warmup {warmup}, steps {steps}")
+    # every call rewrites the same cache rows with the same values, so each step does the same work
+    ms = time_calls(lambda: lib.prefill_chunk(q, kn, vn, kc, vc, wl.pos0, tab, out=out, workspace=ws),
+                    steps, warmup)
+    tf = wl.chunk_flops() / (ms * 1e-3) / 1e12
+    log(f"[bench] chunk prefill: {ms:.4f} ms/step, {tf:.1f} TFLOP/s")
+    return {"c": c, "ms": ms, "tflops": tf}
+
+
 def cpu_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -273,6 +298,8 @@ def main():
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only == "all":
         res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False)
+    if args.only in ("chunk", "all"):
+        res["chunk"] = bench_chunk(lib, inputs, W["chunk"], args.steps, args.warmup)
     if args.only == "long" or (args.only == "all" and not args.no_long):
         res["long"] = bench_prefill(lib, inputs, W["long"], max(3, args.steps // 5), max(2, args.warmup // 5),
                                     variants=False)
@@ -342,6 +369,15 @@ def main():
             "attention_kernel_frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
                        "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale}}
+    if "chunk" in res:
+        r = res["chunk"]
+        wl = r["c"].wl
+        out["chunk_prefill"] = {
+            "value": round(r["tflops"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 5),
+            "frac": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "config": {"workload": "chunked prefill against a KV cache (append, then attend)", "B": wl.B,
+                       "Hq": wl.Hq, "Hkv": wl.Hkv, "chunk_len": wl.S, "pos0": wl.pos0, "S_max": wl.S_max,
+                       "head_dim": wl.D, "flops_per_step": wl.chunk_flops()}}
     if not args.no_cpu_baseline:
         if "prefill" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, prefill sample)")

@@ -144,6 +144,41 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
                                     int table_max_pos, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * attn_prefill_chunk: a chunk of Sq new tokens at positions pos0 .. pos0+Sq-1 of every
+ * sequence is appended to a KV cache, and its queries attend to the whole cache up to
+ * themselves.  The cache keeps earlier tokens' keys and values for reuse (ninaddeshpande.com,
+ * "The KV cache and the memory wall"); prefill in chunks is named on learnllm.online,
+ * "Prefill vs Decode Latency & Memory Wall Waterfall".
+ *
+ * q: [B, Hq, Sq, D] (not yet rotated); k_new, v_new: [B, Hkv, Sq, D] (k_new not yet rotated);
+ * k_cache, v_cache: [B, Hkv, S_max, D], rows [0, pos0) holding the earlier tokens (keys
+ * already rotated, the format attn_decode reads).  All bf16.
+ * Step 1 writes cache rows [pos0, pos0 + Sq): key row s = RoPE(k_new row s - pos0) at
+ *   position s, computed in float32 and rounded to bf16 (nearest even); value rows copied.
+ *   Other cache rows are not modified.
+ * Step 2: o[b, h, i] = softmax over keys j <= pos0 + i of the cache rows [0, pos0 + Sq)
+ *   (the causal mask aligned at the bottom right), the query rotated at position pos0 + i.
+ *   Query head h reads KV head h / (Hq / Hkv).  Scale 1/sqrt(D).
+ * o: [B, Hq, Sq, D] of dtype out_dt; lse: optional float32 [B, Hq, Sq] (natural log).
+ * rope_table: NULL disables RoPE (keys copied into the cache as given, Q.K^T on the exact
+ *   bf16 values); otherwise requires pos0 + Sq <= table_max_pos.
+ * workspace: required with RoPE: at least attn_prefill_workspace_bytes(B, Hkv, pos0 + Sq, D)
+ *   bytes, 16-byte aligned, contents irrelevant.  It receives every key row [0, pos0 + Sq)
+ *   as IEEE half, the Q.K^T operand format (so cached |k| must stay below 6.5e4).
+ * k_new, v_new and q must not overlap the cache.  pos0 = 0 is an ordinary causal prefill whose
+ * keys are kept.
+ * Support matrix: D in {64, 128}; out_dt either.
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers, sizes < 1, pos0 < 0, pos0 + Sq > S_max,
+ * Hq % Hkv != 0, bad RoPE range, missing/small/misaligned workspace with RoPE,
+ * misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                               void* v_cache, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
+                               int Hkv, int Sq, int S_max, int D, int pos0, const float* rope_table,
+                               int table_max_pos, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV
  * cache and the memory wall"), split over the cache length ("split-K") with a merge pass.
  *

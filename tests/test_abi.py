@@ -157,3 +157,30 @@ def test_decode_workspace_geometry():
     assert lib.decode_num_splits(1, 8, 1, 40, 64, 8) == 2
     assert lib.decode_num_splits(1, 8, 1, 1, 64, 0) == 1
     assert lib.decode_workspace_bytes(0, 8, 1, 100, 64, 0) == 0
+
+
+def _chunk(**kw):
+    a = dict(q=A, kn=A, vn=A, kc=A, vc=A, o=A, lse=None, out_dt=BF16, B=2, Hq=8, Hkv=2, Sq=100, S_max=300,
+             D=128, pos0=50, table=A, tmax=300, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = 2 * 2 * (50 + 100) * 128 * 2
+    return lib.raw().attn_prefill_chunk(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["o"], a["lse"], a["out_dt"],
+                                        a["B"], a["Hq"], a["Hkv"], a["Sq"], a["S_max"], a["D"], a["pos0"],
+                                        a["table"], a["tmax"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kn=None), INV), (dict(vn=None), INV), (dict(kc=None), INV),
+    (dict(vc=None), INV), (dict(o=None), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(S_max=0), INV),
+    (dict(D=0), INV), (dict(pos0=-1), INV), (dict(Hq=8, Hkv=3), INV),
+    (dict(pos0=201), INV),                                   # pos0 + Sq > S_max
+    (dict(tmax=149), INV),                                   # table too short for the last position
+    (dict(ws=None), INV), (dict(ws=MIS), INV), (dict(wsb=2 * 2 * 150 * 128 * 2 - 1), INV),
+    (dict(q=MIS), INV), (dict(kc=MIS), INV), (dict(vn=MIS), INV), (dict(lse=MIS), INV),
+    (dict(table=MIS), INV), (dict(D=65), INV), (dict(out_dt=5), INV),
+    (dict(D=96), UNSUP), (dict(D=256, wsb=1 << 30), UNSUP), (dict(D=96, table=None, ws=None), UNSUP),
+])
+def test_prefill_chunk_rejects(kw, code):
+    assert _chunk(**kw) == code

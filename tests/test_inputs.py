@@ -76,3 +76,25 @@ def test_workload_work_counts():
     assert g.prefill_flops() == 2 * 64 * 8192 ** 2 * 128
     d = inputs.WORKLOADS["decode"]
     assert d.decode_kv_bytes() == 1 << 30
+
+
+def test_chunk_workload_and_draw_order():
+    c = inputs.WORKLOADS["chunk"]
+    assert (c.B, c.Hq, c.Hkv, c.S, c.D, c.pos0, c.S_max) == (1, 64, 8, 2048, 128, 6144, 8192)
+    # at pos0 = 0 the count is the ordinary causal prefill's
+    import dataclasses
+    assert dataclasses.replace(c, pos0=0).chunk_flops() == 2 * 64 * 2048 ** 2 * 128
+    assert c.chunk_flops() == 4 * 64 * 128 * (6144 * 2048 + 2048 ** 2 / 2)
+    small = dataclasses.replace(c, S=40, S_max=100, pos0=30, check_rows=8)
+    a = inputs.make_chunk(small)
+    b = inputs.make_chunk(small)
+    assert np.array_equal(a.k_cache.bits, b.k_cache.bits) and np.array_equal(a.rows, b.rows)
+    # draw order q, k_new, v_new, k_cache, v_cache from one PCG64 stream
+    rng = np.random.Generator(np.random.PCG64(small.seed))
+    q = rng.standard_normal((1, 64, 40, 128)).astype(np.float32)
+    assert np.array_equal(a.q.f32, inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(q)))
+    rng.standard_normal((1, 8, 40, 128))
+    rng.standard_normal((1, 8, 40, 128))
+    kc = rng.standard_normal((1, 8, 100, 128)).astype(np.float32)
+    assert np.array_equal(a.k_cache.f32, inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(kc)))
+    assert a.rows.shape == (64, 8)

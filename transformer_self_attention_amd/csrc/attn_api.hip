@@ -119,6 +119,7 @@ attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, f
   a.q = q; a.k = k; a.v = v; a.o = o; a.lse = lse;
   a.out_bf16 = out_dt == ATTN_BF16;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+  a.Sk = S; a.k_rows = S; a.v_rows = S; a.coff = 0;
   a.causal = causal != 0;
   a.pos0 = pos0;
   a.table = rope_table;
@@ -153,11 +154,51 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
   a.q = q; a.k = k_rot; a.v = v; a.o = o; a.lse = lse;
   a.out_bf16 = out_dt == ATTN_BF16;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
+  a.Sk = S; a.k_rows = S; a.v_rows = S; a.coff = 0;
   a.causal = causal != 0;
   a.pos0 = pos0;
   a.table = rope_table;
   a.workspace = nullptr;
   return from_hip(attn::launch_prefill_prerotated(a, k_rot, (hipStream_t)stream));
+}
+
+attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                               void* v_cache, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
+                               int Hkv, int Sq, int S_max, int D, int pos0, const float* rope_table,
+                               int table_max_pos, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !o) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || S_max < 1 || D < 1 || pos0 < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)pos0 + Sq > (int64_t)S_max) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(o) || (lse && !aligned16(lse)))
+    return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0, Sq) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const int Sk = pos0 + Sq;
+  if (rope_table && (!workspace || !aligned16(workspace) ||
+                     workspace_bytes < attn::prefill_workspace_bytes(B, Hkv, Sk, D)))
+    return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * Sq > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+
+  hipStream_t st = (hipStream_t)stream;
+  void* k16 = rope_table ? workspace : nullptr;
+  const hipError_t e = attn::launch_cache_append(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max,
+                                                 D, pos0, rope_table, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  attn::PrefillArgs a;
+  a.q = q; a.k = rope_table ? k16 : k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = Sq; a.D = D;
+  a.causal = true;
+  a.pos0 = pos0;
+  a.table = rope_table;
+  a.workspace = nullptr;
+  a.Sk = Sk; a.k_rows = rope_table ? Sk : S_max; a.v_rows = S_max; a.coff = pos0;
+  return from_hip(attn::launch_prefill_cache(a, st));
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {

@@ -68,11 +68,14 @@ struct PrefillArgs {
   void* o;
   float* lse;
   bool out_bf16;
-  int B, Hq, Hkv, S, D;
+  int B, Hq, Hkv, S, D;  // S: query rows per (batch, head)
   bool causal;
-  int pos0;
+  int pos0;            // RoPE position of query row 0 (and of key row 0 when keys are rotated here)
   const float* table;  // nullptr: no RoPE
   void* workspace;     // bf16 path: room for the rotated fp16 keys, or nullptr (RoPE fused)
+  // Keys: Sk rows per (batch, KV head), stored k_rows / v_rows rows apart (K / V); query row i
+  // sees key j when j <= i + coff.  An ordinary prefill has Sk = k_rows = v_rows = S, coff = 0.
+  int Sk, k_rows, v_rows, coff;
 };
 
 size_t prefill_workspace_bytes(int B, int Hkv, int S, int D);
@@ -81,6 +84,16 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
                                   const float* table, hipStream_t st);
 hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st);
+
+// Chunked prefill against a KV cache (bf16): append the chunk's keys (rotated, rounded to bf16)
+// and values to cache rows [pos0, pos0 + Sq); with RoPE also write every key row [0, pos0 + Sq)
+// as fp16 into k16 ([B*Hkv, pos0 + Sq, D]), the operand format of the Q.K^T product.
+hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                               void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
+                               const float* table, hipStream_t st);
+// The attention of a chunk against the cache: a.k holds the fp16 keys (a.table != nullptr) or
+// the bf16 cache keys (no RoPE).
+hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st);
 
 struct DecodeArgs {
   const void* q;

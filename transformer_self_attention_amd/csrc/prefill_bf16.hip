@@ -29,7 +29,8 @@
 //  * Online softmax in log2 units with lazy rescaling: O and l are rescaled only when a row's max
 //    grows by more than 8 (unnormalised weights stay <= 2^8); normalised once at the end.
 //  * Causal: tiles entirely above a wave's rows are skipped; only tiles crossing the diagonal (or
-//    the tail S) are masked.
+//    the tail of the keys) are masked.  The diagonal may be shifted by coff keys: a chunk of
+//    queries at the end of a longer key sequence (a KV cache) sees every earlier key.
 //  * Workgroup order: heaviest query blocks first; the G query heads sharing one KV head (and the
 //    same query block) go to the same XCD so its L2 serves their K/V reads.
 #include "common.h"
@@ -64,7 +65,8 @@ template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 2, NW / 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
-                         float* __restrict__ lse, int B, int Hq, int Hkv, int S, int pos0,
+                         float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Sk,
+                         int k_rows, int v_rows, int coff, int pos0,
                          const float2* __restrict__ table) {
   constexpr int NT = NW * 64;                // threads per workgroup
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
@@ -88,7 +90,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   // ---- workgroup -> (query block, batch, head) ----
   const int G = Hq / Hkv;
-  const int nqb = (S + BM - 1) / BM;
+  const int nqb = (Sq + BM - 1) / BM;
   const int NG = nqb * B * Hkv;
   const int id = blockIdx.x;
   const int xcd = id % kNumXcd;
@@ -119,8 +121,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   typedef typename std::conditional<QK_BF16, bf16x8, f16x8>::type qk_t;
   qk_t qf[KS];
   {
-    const int rc = row < S ? row : S - 1;
-    const uint16_t* qrow = q + (((int64_t)b * Hq + h) * S + rc) * D;
+    const int rc = row < Sq ? row : Sq - 1;
+    const uint16_t* qrow = q + (((int64_t)b * Hq + h) * Sq + rc) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * hl;
@@ -148,16 +150,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 
   // ---- key range ----
-  const int q_last = min(q0 + BM, S) - 1;
-  const int key_end = CAUSAL ? q_last + 1 : S;
+  // Query row i sees key j when j <= i + coff (coff = 0: the square mask; coff = Sk - Sq: the
+  // mask aligned at the bottom right, for a chunk of queries at the end of the keys).
+  const int q_last = min(q0 + BM, Sq) - 1;
+  const int key_end = CAUSAL ? min(q_last + 1 + coff, Sk) : Sk;
   const int n_tiles = (key_end + kBN - 1) / kBN;
-  const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S * D;
-  const uint16_t* kg = k + kv_off;
-  const uint16_t* vg = v + kv_off;
+  const uint16_t* kg = k + ((int64_t)b * Hkv + hkv) * k_rows * D;
+  const uint16_t* vg = v + ((int64_t)b * Hkv + hkv) * v_rows * D;
   // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
   // [(i * NW + wave) * 64, +64); lane L's chunk P holds logical chunk swz(row, P % NCH)
   // of row P / NCH.  The per-lane element offsets are fixed for the whole kernel; each tile adds
-  // a wave-uniform base.  Rows past S read row S-1 (finite data; those keys are masked).
+  // a wave-uniform base.  Rows past Sk read row Sk-1 (finite data; those keys are masked).
   // Byte offsets are unsigned 32-bit so the loads use the scalar-base + vector-offset form.
   uint32_t dma_byte[DIRECT_PER_WAVE];
   int dma_row[DIRECT_PER_WAVE];
@@ -172,7 +175,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // (operands are formed in locals first: the host compilation pass rejects captured-array
     // elements inside the builtin's argument list and would silently drop the kernel)
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * D);
-    if (k0 + kBN <= S) {
+    if (k0 + kBN <= Sk) {
       // full tile: a buffer resource over the tile (scalar work only) and the fixed per-lane
       // offsets, so no per-lane address arithmetic is repeated per tile
       const __amdgpu_buffer_rsrc_t rsrc =
@@ -187,7 +190,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
       for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
         const int r = dma_row[i];
-        const int rr = min(r, S - 1 - k0);
+        const int rr = min(r, Sk - 1 - k0);
         const uint32_t off = dma_byte[i] - (uint32_t)((r - rr) * D * 2);
         const void* g = base + off;
         ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
@@ -221,7 +224,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + NT * i;
         const int r = c / NCH, cc = c % NCH;
-        const int key = min(k0 + r, S - 1);
+        const int key = min(k0 + r, Sk - 1);
         kst[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * D + cc * 8);
         const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + key) * (D / 2) + cc * 4);
         tst[i][0] = tp[0];
@@ -293,7 +296,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
 
-    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1) {
+    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1 + coff) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
       const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
       // S^T = K Q^T for two 32-key blocks
@@ -321,14 +324,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           for (int r = 0; r < 16; ++r) sacc[kb][r] *= c_log2;
       }
       // mask (diagonal / tail tiles only)
-      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw) || (k0 + kBN > S);
+      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw + coff) || (k0 + kBN > Sk);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if ((CAUSAL && key > row) || key >= S) sacc[kb][r] = -INFINITY;
+            if ((CAUSAL && key > row + coff) || key >= Sk) sacc[kb][r] = -INFINITY;
           }
       }
       bf16x8 pf[2][2];
@@ -456,9 +459,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   // ---- finalize ----
   const float l_tot = l_run + swap_halves(l_run);
-  if (row < S) {
+  if (row < Sq) {
     const float inv = 1.0f / l_tot;
-    const int64_t orow = (((int64_t)b * Hq + h) * S + row) * D;
+    const int64_t orow = (((int64_t)b * Hq + h) * Sq + row) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -475,7 +478,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(o) + orow + d0) = f32x4{o0, o1, o2, o3};
         }
       }
-    if (lse && hl == 0) lse[((int64_t)b * Hq + h) * S + row] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+    if (lse && hl == 0) lse[((int64_t)b * Hq + h) * Sq + row] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   }
 }
 
@@ -517,8 +520,8 @@ hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
-                     (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.pos0,
-                     reinterpret_cast<const float2*>(a.table));
+                     (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.Sk, a.k_rows,
+                     a.v_rows, a.coff, a.pos0, reinterpret_cast<const float2*>(a.table));
   return hipGetLastError();
 }
 
@@ -570,6 +573,12 @@ hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, in
 hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st) {
   return a.D == 64 ? dispatch_mode<64, KMODE_PREROT>(a, k_rot, st)
                    : dispatch_mode<128, KMODE_PREROT>(a, k_rot, st);
+}
+
+hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st) {
+  if (a.table)
+    return a.D == 64 ? dispatch_mode<64, KMODE_PREROT>(a, a.k, st) : dispatch_mode<128, KMODE_PREROT>(a, a.k, st);
+  return a.D == 64 ? dispatch_mode<64, KMODE_RAW>(a, a.k, st) : dispatch_mode<128, KMODE_RAW>(a, a.k, st);
 }
 
 }  // namespace attn

@@ -16,7 +16,7 @@ Recipe (fixed, so every consumer sees the same bits):
 
 Shapes follow the workloads the pages discuss: 2k-token prefill with 32 heads of width
 128, 8k-token GQA with 64 query / 8 KV heads, batch-32 decode over an 8k cache, and a
-32k-token long context.
+32k-token long context; the chunked prefill is the last 2k chunk of the 8k GQA prompt.
 """
 
 from __future__ import annotations
@@ -42,6 +42,8 @@ class Workload:
     big_key_frac: float = 0.0
     big_key_scale: float = 1.0
     rope_base: float = 10000.0
+    pos0: int = 0            # chunk: position of the chunk's first token (cache rows before it are filled)
+    S_max: int = 0           # chunk: cache rows per (sequence, KV head)
 
     @property
     def group(self) -> int:
@@ -55,6 +57,12 @@ class Workload:
         """Bytes a prefill must move at least: read Q, K and V once, write O once."""
         esz = 2 if self.dtype == "bf16" else 4
         return (2 * self.B * self.Hq + 2 * self.B * self.Hkv) * self.S * self.D * esz
+
+    def chunk_flops(self) -> float:
+        """Chunk of S queries after pos0 cached keys: query i meets pos0 + i + 1 keys, counted as
+        4*D per query-key pair with the diagonal half-block, like prefill_flops at pos0 = 0:
+        4*B*Hq*D*(pos0*S + S^2/2)."""
+        return 4.0 * self.B * self.Hq * self.D * (self.pos0 * self.S + self.S * self.S / 2.0)
 
     def decode_kv_bytes(self) -> int:
         """K and V cache bytes one decode step must read."""
@@ -70,6 +78,9 @@ WORKLOADS = {
     "decode": Workload("decode", B=32, Hq=64, Hkv=8, S=8192, D=128, dtype="bf16", seed=3, kind="decode"),
     "long": Workload("long", B=1, Hq=32, Hkv=8, S=32768, D=128, dtype="bf16", seed=4, kind="prefill",
                      check_rows=128, big_key_frac=0.01, big_key_scale=8.0),
+    # the last 2048-token chunk of an 8192-token GQA prompt, against the 6144 tokens already cached
+    "chunk": Workload("chunk", B=1, Hq=64, Hkv=8, S=2048, D=128, dtype="bf16", seed=5, kind="chunk",
+                      check_rows=128, pos0=6144, S_max=8192),
 }
 
 
@@ -186,6 +197,31 @@ def make_prefill(wl: Workload, *, S: Optional[int] = None, B: Optional[int] = No
         k = Tensor(kv, wl.dtype)   # x8 is a power of two: exact after rounding
     rows = np.stack([sample_rows(rng, wl.S, wl.check_rows) for _ in range(wl.Hq)])
     return PrefillInputs(wl, q, k, v, big, rows)
+
+
+@dataclasses.dataclass
+class ChunkInputs:
+    wl: Workload
+    q: Tensor           # [B, Hq, S, D]   the chunk's queries (not rotated)
+    k_new: Tensor       # [B, Hkv, S, D]  the chunk's keys (not rotated)
+    v_new: Tensor       # [B, Hkv, S, D]
+    k_cache: Tensor     # [B, Hkv, S_max, D] cache before the chunk (rows < pos0 used; keys as stored)
+    v_cache: Tensor     # [B, Hkv, S_max, D]
+    rows: np.ndarray    # [Hq, n_rows] checked query rows per head
+
+
+def make_chunk(wl: Workload, *, seed: Optional[int] = None) -> ChunkInputs:
+    """Draw a chunk and the cache it is appended to, in the order q, k_new, v_new, k_cache,
+    v_cache (every cache row is drawn; rows from pos0 on are overwritten by the append)."""
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = Tensor(_normal32(rng, (wl.B, wl.Hq, wl.S, wl.D)), wl.dtype)
+    kn = Tensor(_normal32(rng, (wl.B, wl.Hkv, wl.S, wl.D)), wl.dtype)
+    vn = Tensor(_normal32(rng, (wl.B, wl.Hkv, wl.S, wl.D)), wl.dtype)
+    kc = Tensor(_normal32(rng, (wl.B, wl.Hkv, wl.S_max, wl.D)), wl.dtype)
+    vc = Tensor(_normal32(rng, (wl.B, wl.Hkv, wl.S_max, wl.D)), wl.dtype)
+    rows = np.stack([sample_rows(rng, wl.S, wl.check_rows) for _ in range(wl.Hq)])
+    return ChunkInputs(wl, q, kn, vn, kc, vc, rows)
 
 
 def make_decode(wl: Workload, *, B: Optional[int] = None, S: Optional[int] = None,

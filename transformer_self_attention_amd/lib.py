@@ -29,6 +29,7 @@ EXPORTED = (
     "attn_prefill",
     "attn_rotate_keys_f16",
     "attn_prefill_prerotated",
+    "attn_prefill_chunk",
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
@@ -67,6 +68,9 @@ def _load():
     lib.attn_prefill_prerotated.restype = i32
     lib.attn_prefill_prerotated.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
                                             fp, i32, vp]
+    lib.attn_prefill_chunk.restype = i32
+    lib.attn_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                       fp, i32, vp, sz, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
@@ -237,6 +241,48 @@ def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, out=None, out
     _check(_lib.attn_prefill_prerotated(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(lse), _dt(out), B, Hq,
                                         Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), table.shape[0],
                                         _stream(stream)), "attn_prefill_prerotated")
+    return out
+
+
+def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, out=None, out_dtype=None,
+                  lse=None, workspace=None, stream=None):
+    """Append a chunk (k_new, v_new [B, Hkv, Sq, D]) to the cache [B, Hkv, S_max, D] at rows
+    pos0 .. pos0+Sq-1 (keys rotated there), then attend q [B, Hq, Sq, D] to cache rows
+    [0, pos0 + Sq) with the causal mask aligned at the bottom right.  All bf16.
+
+    workspace: uint8 GPU tensor of >= prefill_workspace_bytes(B, Hkv, pos0 + Sq, D) bytes, needed
+    with RoPE; allocated here when None."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    B, Hq, Sq, D = q.shape
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    if k_new.shape != (B, Hkv, Sq, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, Hkv, Sq, D]")
+    if k_cache.shape != (B, Hkv, S_max, D) or v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache must be [B, Hkv, S_max, D]")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    if lse is not None:
+        _need(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != B * Hq * Sq:
+            raise ValueError("lse must be float32 [B, Hq, Sq]")
+    tmax = 0
+    if table is not None:
+        _need(table, "table")
+        tmax = table.shape[0]
+        if workspace is None:
+            workspace = torch.empty(max(prefill_workspace_bytes(B, Hkv, pos0 + Sq, D), 16), dtype=torch.uint8,
+                                    device=q.device)
+    wsb = 0
+    if workspace is not None:
+        _need(workspace, "workspace")
+        wsb = workspace.numel() * workspace.element_size()
+    _check(_lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                   _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _ptr(table), tmax,
+                                   _ptr(workspace), wsb, _stream(stream)), "attn_prefill_chunk")
     return out
 
 
