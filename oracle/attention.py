@@ -26,6 +26,10 @@ What it computes is the plain definition, written out with NumPy in float64:
   (ninaddeshpande.com), "The KV cache and the memory wall": one new query per sequence
   attends to every cached key.  The cache is used as stored (already rotated); the
   query is rotated at its own position.
+* Paged KV cache -- "Building Self-Attention and Transformer Engines" (codingpancake.com),
+  section 6.2: the cache lives in fixed-size physical blocks (16 tokens on the page) found
+  through a per-sequence table, like virtual-memory pages.  Token t of sequence b is in block
+  block_table[b][t // block_size], slot t % block_size; decode then proceeds as above.
 * Chunked prefill against a cache -- the same page and section (keys and values of
   earlier tokens are kept and reused), with the chunked prefill named on "Multi-Head
   Attention & Rotary Position Embeddings (RoPE)" (learnllm.online), "Prefill vs Decode
@@ -49,7 +53,7 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = ["rope_frequencies", "rope", "attention", "decode", "round_bf16", "append_to_cache",
-           "attention_with_cache"]
+           "attention_with_cache", "decode_paged"]
 
 
 def rope_frequencies(D: int, base: float = 10000.0) -> np.ndarray:
@@ -255,3 +259,28 @@ def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, r
             o[b, h] = w @ vc[b, kv, :Sk]
             lse[b, h] = ls
     return o, lse
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_base=10000.0):
+    """Decode against a paged KV cache.
+
+    k_pages, v_pages: [num_blocks, Hkv, block_size, D] physical blocks; block_table: int
+    [B, max_blocks]; token t of sequence b is stored in block block_table[b, t // block_size] at
+    slot t % block_size.  Sequence b attends to its tokens [0, min(cache_len[b], max_blocks *
+    block_size)).  Other arguments and the result as in decode().
+    """
+    kp = np.asarray(k_pages, dtype=np.float64)
+    vp = np.asarray(v_pages, dtype=np.float64)
+    bt = np.asarray(block_table)
+    B, max_blocks = bt.shape
+    _, Hkv, bs, D = kp.shape
+    S_max = max_blocks * bs
+    kc = np.zeros((B, Hkv, S_max, D))
+    vc = np.zeros((B, Hkv, S_max, D))
+    for b in range(B):
+        L = int(min(max(int(cache_len[b]), 0), S_max))
+        for t in range(L):
+            blk = int(bt[b, t // bs])
+            kc[b, :, t] = kp[blk, :, t % bs]
+            vc[b, :, t] = vp[blk, :, t % bs]
+    return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base)

@@ -1,12 +1,13 @@
 """Pins of the oracle's KV-cache functions (CPU only): bfloat16 rounding of stored keys, the
 append of a chunk to the cache, and a chunk of queries attending to the cache with the causal
-mask aligned at the bottom right.
+mask aligned at the bottom right, and decode against a paged cache.
 
 Passages: the KV cache of "Transformer internals: attention without the mysticism"
 (ninaddeshpande.com), "The KV cache and the memory wall" (earlier tokens' keys and values are
 stored and reused); chunked prefill as named on "Multi-Head Attention & Rotary Position
 Embeddings (RoPE)" (learnllm.online), "Prefill vs Decode Latency & Memory Wall Waterfall"; the
-causal mask of the same page's PyTorch listing.
+causal mask of the same page's PyTorch listing; the paged cache of "Building Self-Attention and
+Transformer Engines" (codingpancake.com), section 6.2.
 """
 
 import math
@@ -14,7 +15,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import append_to_cache, attention, attention_with_cache, decode, rope, round_bf16
+from oracle import append_to_cache, attention, attention_with_cache, decode, decode_paged, rope, round_bf16
 from transformer_self_attention_amd import inputs
 
 
@@ -191,3 +192,77 @@ def test_chunks_in_sequence_build_the_same_cache():
     for a, e in ((0, 5), (5, 6), (6, 17), (17, 23)):
         kc, vc = append_to_cache(kc, vc, k[:, :, a:e], v[:, :, a:e], a)
     assert np.array_equal(kc, whole[0]) and np.array_equal(vc, whole[1])
+
+
+# --------------------------------------------------------------------------------------
+# Paged KV cache (codingpancake.com section 6.2: fixed-size physical blocks and a block table)
+# --------------------------------------------------------------------------------------
+def _pages_from_contiguous(kc, vc, bs, perm, extra_blocks=3):
+    """Scatter a contiguous cache [B, Hkv, S, D] into physical blocks: block j of sequence b goes
+    to physical block perm[b * nb + j]; returns the pools and the block table."""
+    B, Hkv, S, D = kc.shape
+    nb = -(-S // bs)
+    nblk = B * nb + extra_blocks
+    kp = np.full((nblk, Hkv, bs, D), np.nan)
+    vp = np.full((nblk, Hkv, bs, D), np.nan)
+    bt = np.empty((B, nb), dtype=np.int64)
+    for b in range(B):
+        for j in range(nb):
+            phys = int(perm[b * nb + j])
+            bt[b, j] = phys
+            n = min(bs, S - j * bs)
+            kp[phys, :, :n] = kc[b, :, j * bs:j * bs + n]
+            vp[phys, :, :n] = vc[b, :, j * bs:j * bs + n]
+    return kp, vp, bt
+
+
+@pytest.mark.parametrize("bs,shuffle", [(16, False), (16, True), (32, True), (4, True)])
+def test_paged_decode_equals_contiguous_decode(bs, shuffle):
+    B, Hq, Hkv, S, D = 3, 8, 2, 80, 16
+    kc, vc, q = _rand((B, Hkv, S, D), 60), _rand((B, Hkv, S, D), 61), _rand((B, Hq, 1, D), 62)
+    nb = -(-S // bs)
+    perm = np.random.default_rng(63).permutation(B * nb + 3) if shuffle else np.arange(B * nb + 3)
+    kp, vp, bt = _pages_from_contiguous(kc, vc, bs, perm)
+    lens = [80, 37, 1]
+    qpos = [80, 40, 3]
+    o, lse = decode_paged(q, kp, vp, bt, lens, qpos)
+    o_ref, lse_ref = decode(q, kc, vc, lens, qpos)
+    assert np.array_equal(o, o_ref) and np.array_equal(lse, lse_ref)
+    # unused pool slots hold NaN: none of them is read
+    assert np.all(np.isfinite(o))
+
+
+def test_paged_decode_ignores_table_entries_past_the_length():
+    B, Hq, Hkv, S, D, bs = 2, 4, 1, 64, 8, 16
+    kc, vc, q = _rand((B, Hkv, S, D), 70), _rand((B, Hkv, S, D), 71), _rand((B, Hq, 1, D), 72)
+    kp, vp, bt = _pages_from_contiguous(kc, vc, bs, np.arange(B * 4 + 3))
+    bt[0, 2:] = 10 ** 9        # sequence 0 uses 2 blocks (length 20 -> blocks 0, 1)
+    bt[1, 1:] = -5             # sequence 1 uses 1 block (length 16)
+    o, _ = decode_paged(q, kp, vp, bt, [20, 16], [20, 16])
+    o_ref, _ = decode(q, kc, vc, [20, 16], [20, 16])
+    assert np.array_equal(o, o_ref)
+
+
+def test_paged_decode_brute_force_tiny():
+    """Scalar loops reading the blocks directly (no contiguous cache is formed)."""
+    Hq, Hkv, D, bs = 4, 2, 8, 4
+    kp, vp = _rand((7, Hkv, bs, D), 80), _rand((7, Hkv, bs, D), 81)
+    q = _rand((1, Hq, 1, D), 82)
+    bt = np.array([[5, 0, 3]])
+    L, pos = 10, 12
+    o, _ = decode_paged(q, kp, vp, bt, [L], [pos])
+    G = Hq // Hkv
+    for h in range(Hq):
+        kv = h // G
+        qi = list(q[0, h, 0])
+        for p in range(D // 2):
+            ang = pos * 10000.0 ** (-(2.0 * p) / D)
+            c, s = math.cos(ang), math.sin(ang)
+            qi[2 * p], qi[2 * p + 1] = q[0, h, 0, 2 * p] * c - q[0, h, 0, 2 * p + 1] * s, \
+                q[0, h, 0, 2 * p] * s + q[0, h, 0, 2 * p + 1] * c
+        sc = [sum(qi[d] * kp[bt[0, t // bs], kv, t % bs, d] for d in range(D)) / math.sqrt(D) for t in range(L)]
+        mx = max(sc)
+        w = [math.exp(x - mx) for x in sc]
+        den = sum(w)
+        want = [sum(w[t] / den * vp[bt[0, t // bs], kv, t % bs, d] for t in range(L)) for d in range(D)]
+        assert np.allclose(o[0, h, 0], want, atol=1e-13)
