@@ -14,6 +14,8 @@ One step = one pass of the hot path over the workload's synthetic batch:
   * MHA (sub-object ``mha_prefill``): B=4, H=32, S=2048, D=128 prefill, same step.
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
     key rows scaled by 8.
+  * paged decode (sub-object ``paged_decode``): the decode workload with the cache cut into
+    16-token blocks scattered over a pool in a seeded random order; one attn_decode_paged call.
   * chunk (sub-object ``chunk_prefill``): the last 2048-token chunk of an 8192-token GQA prompt
     (B=1, Hq=64, Hkv=8, D=128) against the 6144 tokens already in the KV cache; one
     attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
@@ -93,7 +95,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "long", "chunk", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "all"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -193,6 +195,27 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
     n_split = lib.decode_num_splits(wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, 0)
     return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
+
+
+def bench_paged_decode(lib, inputs, wl, steps, warmup, block_size=16):
+    import torch
+    log(f"[bench] generating paged decode inputs B={wl.B} cache={wl.S} block={block_size}")
+    pd = inputs.make_paged_decode(wl, block_size=block_size)
+    q, kp, vp = pd.q.torch("cuda"), pd.k_pages.torch("cuda"), pd.v_pages.torch("cuda")
+    bt = torch.from_numpy(pd.block_table).cuda()
+    cl = torch.from_numpy(pd.cache_len).cuda()
+    qp = torch.from_numpy(pd.q_pos).cuda()
+    tab = lib.make_rope_table(int(pd.q_pos.max()) + 1, wl.D)
+    out = torch.empty_like(q)
+    ws = torch.empty(lib.decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, bt.shape[1] * block_size, wl.D, 0),
+                     dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] timing paged decode: warmup {warmup}, steps {steps}")
+    ms = time_calls(lambda: lib.decode_paged(q, kp, vp, bt, cl, qp, tab, out=out, workspace=ws), steps, warmup)
+    gbs = wl.decode_kv_bytes() / (ms * 1e-3) / 1e9
+    log(f"[bench] paged decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
+    return {"ms": ms, "gbs": gbs, "block_size": block_size, "num_blocks": int(pd.k_pages.shape[0]),
+            "steps": steps, "warmup": warmup, "wl": wl}
 
 
 def bench_chunk(lib, inputs, wl, steps, warmup):
@@ -298,6 +321,8 @@ def main():
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only == "all":
         res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False)
+    if args.only in ("paged", "all"):
+        res["paged"] = bench_paged_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("chunk", "all"):
         res["chunk"] = bench_chunk(lib, inputs, W["chunk"], args.steps, args.warmup)
     if args.only == "long" or (args.only == "all" and not args.no_long):
@@ -369,6 +394,16 @@ def main():
             "attention_kernel_frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
                        "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale}}
+    if "paged" in res:
+        r = res["paged"]
+        wl = r["wl"]
+        out["paged_decode"] = {
+            "value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 5),
+            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "steps": r["steps"], "warmup": r["warmup"],
+            "config": {"workload": "batch decode against a paged KV cache (blocks scattered over a pool)",
+                       "B": wl.B, "cache_len": wl.S, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D,
+                       "block_size": r["block_size"], "num_blocks": r["num_blocks"],
+                       "kv_bytes_per_step": wl.decode_kv_bytes()}}
     if "chunk" in res:
         r = res["chunk"]
         wl = r["c"].wl

@@ -205,6 +205,33 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         int D, const float* rope_table, int table_max_pos, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------------------
+ * attn_decode_paged: attn_decode against a paged KV cache.  The cache is a pool of
+ * fixed-size physical blocks, allocated on demand and found through a per-sequence block
+ * table like virtual-memory pages ("Building Self-Attention and Transformer Engines",
+ * codingpancake.com, section 6.2; the page uses 16 tokens per block).
+ *
+ * k_pages, v_pages: [num_blocks, Hkv, block_size, D], keys already rotated (used as stored).
+ * block_table: device int32 [B, max_blocks]; token t of sequence b is stored in block
+ *   block_table[b * max_blocks + t / block_size], slot t % block_size.  Only the entries of
+ *   blocks holding tokens [0, cache_len[b]) are read; the rest may hold anything.  An entry
+ *   read outside [0, num_blocks) is clamped into it (no out-of-range access; the result is
+ *   then meaningless).
+ * cache_len, q_pos, q, o, lse, n_split, rope_table: as in attn_decode, with
+ *   S_max = max_blocks * block_size (cache_len is clamped to it).
+ * workspace: at least attn_decode_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, D,
+ *   n_split) bytes.
+ * Support matrix: as attn_decode; block_size a power of two in [16, 4096].
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers, sizes < 1, a bad block_size, Hq % Hkv != 0,
+ * workspace too small, misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int num_blocks,
+                              int block_size, const int32_t* block_table, int max_blocks,
+                              const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                              attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int D,
+                              const float* rope_table, int table_max_pos, int n_split, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

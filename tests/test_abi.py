@@ -184,3 +184,28 @@ def _chunk(**kw):
 ])
 def test_prefill_chunk_rejects(kw, code):
     assert _chunk(**kw) == code
+
+
+def _paged(**kw):
+    a = dict(q=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=64, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16,
+             B=4, Hq=16, Hkv=2, D=128, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], max(a["mb"] * a["bs"], 1),
+                                              max(a["D"], 1), max(a["ns"], 0))
+    return lib.raw().attn_decode_paged(a["q"], a["kp"], a["vp"], a["nblk"], a["bs"], a["bt"], a["mb"], a["cl"],
+                                       a["qp"], a["o"], a["lse"], a["in_dt"], a["out_dt"], a["B"], a["Hq"], a["Hkv"],
+                                       a["D"], a["table"], a["tmax"], a["ns"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kp=None), INV), (dict(vp=None), INV), (dict(bt=None), INV), (dict(cl=None), INV),
+    (dict(o=None), INV), (dict(ws=None), INV), (dict(qp=None), INV),
+    (dict(B=0), INV), (dict(Hq=15), INV), (dict(nblk=0), INV), (dict(mb=0), INV), (dict(ns=-1), INV),
+    (dict(bs=8), INV), (dict(bs=24), INV), (dict(bs=0), INV), (dict(bs=8192), INV),
+    (dict(wsb=16), INV), (dict(kp=MIS), INV), (dict(ws=MIS), INV), (dict(bt=P(0x10002)), INV),
+    (dict(cl=P(0x10002)), INV), (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
+    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+])
+def test_decode_paged_rejects(kw, code):
+    assert _paged(**kw) == code

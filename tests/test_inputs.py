@@ -98,3 +98,24 @@ def test_chunk_workload_and_draw_order():
     kc = rng.standard_normal((1, 8, 100, 128)).astype(np.float32)
     assert np.array_equal(a.k_cache.f32, inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(kc)))
     assert a.rows.shape == (64, 8)
+
+
+def test_paged_decode_layout():
+    """Each table entry points at the pool block holding those tokens; other slots are NaN."""
+    wl = inputs.Workload("d", B=3, Hq=8, Hkv=2, S=70, D=16, dtype="bf16", seed=9, kind="decode")
+    pd = inputs.make_paged_decode(wl, block_size=16, spare_blocks=4)
+    d = pd.contiguous
+    assert pd.block_table.shape == (3, 5) and pd.k_pages.shape == (19, 2, 16, 16)
+    assert len(set(pd.block_table.ravel().tolist())) == 15
+    for b in range(3):
+        for t in range(70):
+            blk = pd.block_table[b, t // 16]
+            assert np.array_equal(pd.k_pages.bits[blk, :, t % 16], d.k_cache.bits[b, :, t])
+            assert np.array_equal(pd.v_pages.bits[blk, :, t % 16], d.v_cache.bits[b, :, t])
+    used = np.zeros(19, bool)
+    used[pd.block_table.ravel()] = True
+    assert np.all(np.isnan(pd.k_pages.f32[~used]))
+    assert np.all(np.isnan(pd.k_pages.f32[pd.block_table[:, 4], :, 6:]))   # tail of the last block
+    # same draws as the contiguous generator
+    d2 = inputs.make_decode(wl)
+    assert np.array_equal(d.k_cache.bits, d2.k_cache.bits) and np.array_equal(d.q.bits, d2.q.bits)

@@ -253,6 +253,57 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   const size_t parts = (size_t)B * Hq * ns;
   a.ws_o = static_cast<float*>(workspace);
   a.ws_ml = static_cast<float*>(workspace) + parts * D;
+  a.block_table = nullptr;
+  a.max_blocks = 0; a.bs_log2 = 0; a.num_blocks = 0;
+  return from_hip(attn::launch_decode(a, (hipStream_t)stream));
+}
+
+attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int num_blocks,
+                              int block_size, const int32_t* block_table, int max_blocks,
+                              const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                              attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int D,
+                              const float* rope_table, int table_max_pos, int n_split, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!q || !k_pages || !v_pages || !block_table || !cache_len || !o || !workspace) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && !q_pos) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || num_blocks < 1 || max_blocks < 1 || n_split < 0)
+    return ATTN_ERR_INVALID_ARG;
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks * block_size > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) || !aligned16(workspace) ||
+      (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (q_pos && (reinterpret_cast<uintptr_t>(q_pos) & 3u)))
+    return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (!aligned16(rope_table) || table_max_pos < 1)) return ATTN_ERR_INVALID_ARG;
+  const int S_max = max_blocks * block_size;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split)) return ATTN_ERR_INVALID_ARG;
+  if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * Hkv * block_size * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+
+  int ns, chunk;
+  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  attn::DecodeArgs a;
+  a.q = q; a.k = k_pages; a.v = v_pages;
+  a.cache_len = cache_len; a.q_pos = q_pos;
+  a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_max = S_max; a.D = D;
+  a.table = rope_table; a.table_max_pos = table_max_pos;
+  a.n_split = ns; a.chunk = chunk;
+  const size_t parts = (size_t)B * Hq * ns;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = static_cast<float*>(workspace) + parts * D;
+  a.block_table = block_table;
+  a.max_blocks = max_blocks;
+  int lg = 0;
+  while ((1 << lg) < block_size) ++lg;
+  a.bs_log2 = lg;
+  a.num_blocks = num_blocks;
   return from_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 

@@ -111,6 +111,11 @@ struct DecodeArgs {
   int chunk;           // keys per split (multiple of the kernel's key block)
   float* ws_o;         // [B, Hq, n_split, D]
   float* ws_ml;        // [B, Hq, n_split, 2]
+  // Paged cache (block_table != nullptr): k and v are pools [num_blocks, Hkv, 1 << bs_log2, D];
+  // token t of sequence b is in block block_table[b * max_blocks + (t >> bs_log2)];
+  // S_max = max_blocks << bs_log2.
+  const int32_t* block_table;
+  int max_blocks, bs_log2, num_blocks;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);

@@ -24,6 +24,13 @@
 //    lse directly; otherwise (4 waves per workgroup) it writes one partial per (row, split).
 // decode_merge_kernel, one workgroup per (sequence, query head), only after a split cache:
 // combines the splits with the same log-sum-exp algebra and writes o and lse.
+//
+// Paged cache (PAGED): the cache is a pool of fixed-size blocks [num_blocks, Hkv, bs, D] found
+// through a per-sequence block table (codingpancake.com "Building Self-Attention and Transformer
+// Engines", section 6.2).  bs is a power of two >= 16, so each 16-key half of a wave's 32-key
+// sub-block lies in one block: the two block ids are wave-uniform scalars, fetched one sub-block
+// ahead of the loads that use them, and every lane's K/V address is the block's base plus its
+// slot, exactly as in the contiguous cache.
 #include "common.h"
 
 namespace attn {
@@ -60,12 +67,13 @@ __device__ __forceinline__ int vswz(int r, int lc) {  // 16 chunks per row (D = 
 // NW waves per workgroup.  WHOLE: one split covers the whole cache, and the workgroup writes the
 // final o (OUT_BF16 selects its type) and lse itself; otherwise it writes one partial (m, l, O)
 // per (row, split) for decode_merge_kernel.
-template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16>
+template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16, bool PAGED>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int Hq, int Hkv,
     int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
-    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse) {
+    float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse,
+    const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks) {
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * 64;
   constexpr int NCH = D / 8;
@@ -131,9 +139,25 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     }
   }
 
-  const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S_max * D;
+  // contiguous: rows of this (sequence, KV head); paged: the block pool (rows found per block)
+  const int64_t kv_off = PAGED ? 0 : ((int64_t)b * Hkv + hkv) * S_max * D;
   const uint16_t* kg = kc + kv_off;
   const uint16_t* vg = vc + kv_off;
+  const int32_t* btr = block_table + (PAGED ? (int64_t)b * max_blocks : 0);
+  const int bmask = (1 << bs_log2) - 1;
+  // Paged: pool row of the first key of each 16-key half of the sub-block at k0 (a half past the
+  // end of the cache reuses the first half's block, so every address stays inside a block).
+  auto half_rows = [&](int k0, int64_t& r0, int64_t& r1) {
+    const int k0u = wave_uniform(k0);
+    int blk0 = wave_uniform(btr[k0u >> bs_log2]);
+    int blk1 = blk0;
+    const int k1 = k0u + 16;
+    if (k1 < kend) blk1 = wave_uniform(btr[k1 >> bs_log2]);
+    blk0 = min(max(blk0, 0), num_blocks - 1);
+    blk1 = min(max(blk1, 0), num_blocks - 1);
+    r0 = (((int64_t)blk0 * Hkv + hkv) << bs_log2) + (k0u & bmask);
+    r1 = k1 < kend ? (((int64_t)blk1 * Hkv + hkv) << bs_log2) + (k1 & bmask) : r0;
+  };
 
   f32x4 oacc[DB];
 #pragma unroll
@@ -143,12 +167,16 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // K: lane loads key (kb*16 + i16), 16 B at d = 32 ks + 8 g16  -> A operand directly.
   // V: lane loads chunk c = lane + 64 i of the 32 x D tile (row c / NCH, chunk c % NCH).
   u32x4 kst[2][KS], vst[LPT];
-  auto issue = [&](int k0) {
+  // r0, r1: paged only (pool rows of the two halves); the contiguous cache ignores them.
+  auto issue = [&](int k0, int64_t r0, int64_t r1) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = k0 + kb * 16 + i16;
       const bool ok = key < kend;
-      const uint16_t* kp = kg + (int64_t)(ok ? key : kbeg) * D + 8 * g16;
+      int64_t row;
+      if constexpr (PAGED) row = ok ? (kb ? r1 : r0) + i16 : r0;
+      else row = ok ? key : kbeg;
+      const uint16_t* kp = kg + row * D + 8 * g16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kst[kb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * ks));
     }
@@ -157,7 +185,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       const int c = lane + 64 * i;
       const int key = k0 + c / NCH;
       const bool ok = key < kend;
-      vst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + (int64_t)(ok ? key : kbeg) * D + (c % NCH) * 8));
+      int64_t row;
+      if constexpr (PAGED) row = ok ? ((c / NCH) >= 16 ? r1 : r0) + ((c / NCH) & 15) : r0;
+      else row = ok ? key : kbeg;
+      vst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + row * D + (c % NCH) * 8));
       if (!ok) vst[i] = u32x4{0, 0, 0, 0};
     }
   };
@@ -165,7 +196,14 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   ATTN_LDS uint16_t* vl = (ATTN_LDS uint16_t*)(v_lds[wave]);
   const int nsub = kend > kbeg ? (kend - kbeg + kSub - 1) / kSub : 0;
   int it = wave;
-  if (it < nsub) issue(kbeg + it * kSub);
+  int64_t nr0 = 0, nr1 = 0;  // paged: pool rows of the next sub-block to issue
+  if constexpr (PAGED) {
+    if (it < nsub) half_rows(kbeg + it * kSub, nr0, nr1);
+  }
+  if (it < nsub) issue(kbeg + it * kSub, nr0, nr1);
+  if constexpr (PAGED) {
+    if (it + kWaves < nsub) half_rows(kbeg + (it + kWaves) * kSub, nr0, nr1);
+  }
   for (; it < nsub; it += kWaves) {
     const int k0 = kbeg + it * kSub;
     // consume staged registers
@@ -181,7 +219,13 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       const int off = r * D + (D == 128 ? vswz(r, cc) : (cc ^ (r & 7))) * 8;
       *reinterpret_cast<ATTN_LDS u32x4*>(vl + off) = vst[i];
     }
-    if (it + kWaves < nsub) issue(k0 + kWaves * kSub);
+    if (it + kWaves < nsub) {
+      issue(k0 + kWaves * kSub, nr0, nr1);
+      // the block ids of the sub-block after that are fetched now, a whole iteration ahead
+      if constexpr (PAGED) {
+        if (it + 2 * kWaves < nsub) half_rows(k0 + 2 * kWaves * kSub, nr0, nr1);
+      }
+    }
 
     // scores
     f32x4 sacc[2];
@@ -323,7 +367,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   if (lse && d == 0) lse[(int64_t)b * Hq + h] = ls;
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool PAGED>
 hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* kc = (const uint16_t*)a.k;
@@ -332,18 +376,21 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   if (a.n_split == 1) {
     // one workgroup per (sequence, KV head) streams the whole cache and writes o itself
     if (a.out_bf16)
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true>), dim3(1, a.Hkv, a.B),
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED>), dim3(1, a.Hkv, a.B),
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
-                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
+                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
+                         a.max_blocks, a.bs_log2, a.num_blocks);
     else
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false>), dim3(1, a.Hkv, a.B),
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED>), dim3(1, a.Hkv, a.B),
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
-                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
+                         tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
+                         a.max_blocks, a.bs_log2, a.num_blocks);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false>), dim3(a.n_split, a.Hkv, a.B),
-                     dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max, tab,
-                     a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse);
+  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED>),
+                     dim3(a.n_split, a.Hkv, a.B), dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
+                     a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse,
+                     a.block_table, a.max_blocks, a.bs_log2, a.num_blocks);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.out_bf16)
@@ -355,12 +402,17 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool PAGED>
+hipError_t go_d(const DecodeArgs& a, hipStream_t st) {
+  const bool rope = a.table != nullptr;
+  if (a.D == 64) return rope ? go<64, true, PAGED>(a, st) : go<64, false, PAGED>(a, st);
+  return rope ? go<128, true, PAGED>(a, st) : go<128, false, PAGED>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const bool rope = a.table != nullptr;
-  if (a.D == 64) return rope ? go<64, true>(a, st) : go<64, false>(a, st);
-  return rope ? go<128, true>(a, st) : go<128, false>(a, st);
+  return a.block_table ? go_d<true>(a, st) : go_d<false>(a, st);
 }
 
 }  // namespace attn

@@ -110,6 +110,14 @@ class Tensor:
         else:
             raise ValueError(dtype)
 
+    @classmethod
+    def from_bf16_bits(cls, bits: np.ndarray) -> "Tensor":
+        t = cls.__new__(cls)
+        t.dtype = "bf16"
+        t.bits = np.ascontiguousarray(bits, dtype=np.uint16)
+        t.f32 = bf16_bits_to_f32(t.bits)
+        return t
+
     @property
     def shape(self):
         return self.f32.shape
@@ -239,3 +247,48 @@ def make_decode(wl: Workload, *, B: Optional[int] = None, S: Optional[int] = Non
     if q_pos is None:
         q_pos = np.asarray(cache_len, dtype=np.int32).copy()
     return DecodeInputs(wl, q, kc, vc, np.asarray(cache_len, dtype=np.int32), np.asarray(q_pos, dtype=np.int32))
+
+
+BF16_NAN_BITS = 0x7FC0
+
+
+@dataclasses.dataclass
+class PagedDecodeInputs:
+    wl: Workload
+    q: Tensor                 # [B, Hq, 1, D]
+    k_pages: Tensor           # [num_blocks, Hkv, block_size, D]
+    v_pages: Tensor
+    block_table: np.ndarray   # int32 [B, max_blocks]
+    cache_len: np.ndarray     # int32 [B]
+    q_pos: np.ndarray         # int32 [B]
+    block_size: int
+    contiguous: DecodeInputs  # the same cache, unpaged
+
+
+def make_paged_decode(wl: Workload, *, block_size: int = 16, spare_blocks: int = 5, seed: Optional[int] = None,
+                      cache_len=None, q_pos=None) -> PagedDecodeInputs:
+    """The decode inputs of make_decode (same draws), with the cache cut into blocks of
+    block_size tokens scattered over a pool in a seeded random order (as blocks allocated on
+    demand end up).  Pool blocks that belong to no sequence (spare_blocks of them, plus the
+    unused tail of each sequence's last block) hold bf16 NaN, so reading one shows in the result.
+    The layout draws come from their own stream (seed + 1000003), after nothing else."""
+    d = make_decode(wl, seed=seed, cache_len=cache_len, q_pos=q_pos)
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed + 1000003))
+    B, Hkv, S, D = wl.B, wl.Hkv, wl.S, wl.D
+    nb = -(-S // block_size)
+    num_blocks = B * nb + spare_blocks
+    perm = rng.permutation(num_blocks)
+    table = perm[:B * nb].reshape(B, nb).astype(np.int32)
+
+    def scatter(bits):
+        pool = np.full((num_blocks, Hkv, block_size, D), BF16_NAN_BITS, dtype=np.uint16)
+        padded = np.full((B, Hkv, nb * block_size, D), BF16_NAN_BITS, dtype=np.uint16)
+        padded[:, :, :S] = bits
+        blocks = padded.reshape(B, Hkv, nb, block_size, D).transpose(0, 2, 1, 3, 4).reshape(B * nb, Hkv,
+                                                                                            block_size, D)
+        pool[perm[:B * nb]] = blocks
+        return Tensor.from_bf16_bits(pool)
+
+    return PagedDecodeInputs(wl, d.q, scatter(d.k_cache.bits), scatter(d.v_cache.bits), table, d.cache_len,
+                             d.q_pos, block_size, d)

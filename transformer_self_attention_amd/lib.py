@@ -33,6 +33,7 @@ EXPORTED = (
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
+    "attn_decode_paged",
 )
 
 
@@ -78,6 +79,9 @@ def _load():
     lib.attn_decode.restype = i32
     lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, fp,
                                 i32, i32, vp, sz, vp]
+    lib.attn_decode_paged.restype = i32
+    lib.attn_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
+                                      fp, i32, i32, vp, sz, vp]
     return lib
 
 
@@ -324,4 +328,45 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, out=
                             _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _ptr(table), tmax,
                             n_split, _ptr(workspace), workspace.numel() * workspace.element_size(),
                             _stream(stream)), "attn_decode")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None, *, n_split=0, out=None,
+                 out_dtype=None, lse=None, workspace=None, stream=None):
+    """decode() against a paged cache: pools [num_blocks, Hkv, block_size, D] and an int32 block
+    table [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size])."""
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
+                 (cache_len, "cache_len")):
+        _need(t, n)
+    B, Hq, one, D = q.shape
+    if one != 1:
+        raise ValueError("q must be [B, Hq, 1, D]")
+    num_blocks, Hkv, bs, _ = k_pages.shape
+    if v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must match")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    max_blocks = block_table.shape[1]
+    if cache_len.dtype != torch.int32 or cache_len.numel() != B:
+        raise ValueError("cache_len must be int32 [B]")
+    if q_pos is not None:
+        _need(q_pos, "q_pos")
+        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
+            raise ValueError("q_pos must be int32 [B]")
+    if out is None:
+        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    need = decode_workspace_bytes(B, Hq, Hkv, max_blocks * bs, D, n_split)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    tmax = 0
+    if table is not None:
+        _need(table, "table")
+        tmax = table.shape[0]
+    _check(_lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_blocks, bs, _ptr(block_table),
+                                  max_blocks, _ptr(cache_len), _ptr(q_pos), _ptr(out), _ptr(lse), _dt(q), _dt(out),
+                                  B, Hq, Hkv, D, _ptr(table), tmax, n_split, _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+           "attn_decode_paged")
     return out
