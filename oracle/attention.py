@@ -30,6 +30,10 @@ What it computes is the plain definition, written out with NumPy in float64:
   section 6.2: the cache lives in fixed-size physical blocks (16 tokens on the page) found
   through a per-sequence table, like virtual-memory pages.  Token t of sequence b is in block
   block_table[b][t // block_size], slot t % block_size; decode then proceeds as above.
+* Sliding window -- "Building Self-Attention and Transformer Engines" (codingpancake.com),
+  section 6.4: each token attends only to the W tokens before it (W = 4096 on the page).  The
+  reading taken: the query at position p sees the keys at positions p - W .. p (the W preceding
+  tokens and itself), on top of the causal mask.  window=None means no window.
 * Chunked prefill against a cache -- the same page and section (keys and values of
   earlier tokens are kept and reused), with the chunked prefill named on "Multi-Head
   Attention & Rotary Position Embeddings (RoPE)" (learnllm.online), "Prefill vs Decode
@@ -88,6 +92,11 @@ def rope(x: np.ndarray, positions, base: float = 10000.0) -> np.ndarray:
     return out
 
 
+def _check_window(window, causal):
+    if window is not None and (window < 0 or not causal):
+        raise ValueError("a window is a non-negative key count, used with the causal mask")
+
+
 def _softmax_rows(scores: np.ndarray):
     """Row-wise softmax of devthesis section 1 with the row max subtracted (exact in real arithmetic).
 
@@ -105,12 +114,13 @@ def _softmax_rows(scores: np.ndarray):
     return w, lse[..., 0]
 
 
-def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0, rows=None):
+def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0, rows=None, window=None):
     """Prefill attention over [B, H, S, D] tensors, materialising every score row.
 
     q: [B, Hq, S, D]; k, v: [B, Hkv, S, D] (float64 or anything castable).
     rope_base: None disables RoPE; otherwise Q and K rows are rotated at positions pos0 + s.
     causal: key j is visible to query row i only if j <= i (square mask aligned at the top left).
+    window: None, or W >= 0 (causal only): key j is visible to row i only if j >= i - W.
     rows: None for every row, or an int array [Hq, n] of query rows to compute per head.
     Returns (o, lse): o [B, Hq, n, D], lse [B, Hq, n] (natural log of the softmax normaliser of
     the scaled scores).
@@ -120,6 +130,7 @@ def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0,
     v = np.asarray(v, dtype=np.float64)
     B, Hq, S, D = q.shape
     Hkv = k.shape[1]
+    _check_window(window, causal)
     if Hq % Hkv:
         raise ValueError("Hq must be a multiple of Hkv")
     G = Hq // Hkv
@@ -144,18 +155,22 @@ def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0,
             s = (qh @ k_rot[kv].T) * scale                  # [n, S] full rows
             if causal:
                 s = np.where(keys[None, :] > r[:, None], -np.inf, s)
+            if window is not None:
+                s = np.where(keys[None, :] < r[:, None] - window, -np.inf, s)
             w, ls = _softmax_rows(s)
             o[b, h] = w @ v[b, kv]
             lse[b, h] = ls
     return o, lse
 
 
-def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0):
+def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0, window=None):
     """One query per sequence against a KV cache (keys already rotated; used as stored).
 
     q: [B, Hq, 1, D]; k_cache, v_cache: [B, Hkv, S_max, D]; cache_len, q_pos: [B] ints.
     Query head h of sequence b is rotated at q_pos[b] and attends to cache rows
-    [0, min(cache_len[b], S_max)); cache_len <= 0 gives o = 0 and lse = -inf.
+    [0, min(cache_len[b], S_max)); cache_len <= 0 gives o = 0 and lse = -inf.  Cache row j holds
+    the token at position j; with a window W only rows j >= q_pos[b] - W are visible (none
+    visible: o = 0, lse = -inf).
     Returns (o [B, Hq, 1, D], lse [B, Hq]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -167,9 +182,11 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0):
     scale = 1.0 / np.sqrt(D)
     o = np.zeros((B, Hq, 1, D))
     lse = np.full((B, Hq), -np.inf)
+    _check_window(window, True)
     for b in range(B):
         L = int(min(max(int(cache_len[b]), 0), S_max))
-        if L == 0:
+        lo = 0 if window is None else max(0, int(q_pos[b]) - window)
+        if lo >= L:
             continue
         qb = q[b, :, 0, :]                                   # [Hq, D]
         if rope_base is not None:
@@ -177,6 +194,7 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0):
         for kv in range(Hkv):
             qg = qb[kv * G:(kv + 1) * G]                     # [G, D]
             s = (qg @ kc[b, kv, :L].T) * scale               # [G, L]
+            s[:, :lo] = -np.inf                              # outside the window
             w, ls = _softmax_rows(s)
             o[b, kv * G:(kv + 1) * G, 0, :] = w @ vc[b, kv, :L]
             lse[b, kv * G:(kv + 1) * G] = ls
@@ -219,12 +237,13 @@ def append_to_cache(k_cache, v_cache, k_new, v_new, pos0: int, *, rope_base=1000
     return kc, vc
 
 
-def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, rows=None):
+def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, rows=None, window=None):
     """A chunk of Sq queries at positions pos0 .. pos0+Sq-1 against the cache rows [0, pos0 + Sq).
 
     q: [B, Hq, Sq, D] (rotated here at pos0 + i unless rope_base is None); k_cache, v_cache:
     [B, Hkv, S_max, D] used as stored (the chunk's own keys already appended).  Query i sees
-    key j only if j <= pos0 + i.  rows: None for every row, or an int array [Hq, n].
+    key j only if j <= pos0 + i (and, with a window W, j >= pos0 + i - W).  rows: None for every
+    row, or an int array [Hq, n].
     Returns (o [B, Hq, n, D], lse [B, Hq, n]).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -237,6 +256,7 @@ def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, r
     Sk = pos0 + Sq
     if pos0 < 0 or Sk > kc.shape[2]:
         raise ValueError("chunk does not fit the cache")
+    _check_window(window, True)
     G = Hq // Hkv
     if rows is None:
         rows = np.broadcast_to(np.arange(Sq), (Hq, Sq))
@@ -255,13 +275,15 @@ def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, r
                 qh = rope(qh, pos0 + r, rope_base)
             s = (qh @ kc[b, kv, :Sk].T) * scale                  # [n, pos0 + Sq] full rows
             s = np.where(keys[None, :] > pos0 + r[:, None], -np.inf, s)
+            if window is not None:
+                s = np.where(keys[None, :] < pos0 + r[:, None] - window, -np.inf, s)
             w, ls = _softmax_rows(s)
             o[b, h] = w @ vc[b, kv, :Sk]
             lse[b, h] = ls
     return o, lse
 
 
-def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_base=10000.0):
+def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_base=10000.0, window=None):
     """Decode against a paged KV cache.
 
     k_pages, v_pages: [num_blocks, Hkv, block_size, D] physical blocks; block_table: int
@@ -283,4 +305,4 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_bas
             blk = int(bt[b, t // bs])
             kc[b, :, t] = kp[blk, :, t % bs]
             vc[b, :, t] = vp[blk, :, t % bs]
-    return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base)
+    return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base, window=window)
