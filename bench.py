@@ -16,6 +16,8 @@ One step = one pass of the hot path over the workload's synthetic batch:
     key rows scaled by 8.
   * paged decode (sub-object ``paged_decode``): the decode workload with the cache cut into
     16-token blocks scattered over a pool in a seeded random order; one attn_decode_paged call.
+  * sliding window (sub-objects ``swa_prefill``, ``swa_decode``): the long-context prefill and
+    the decode workload with a 4096-token window (a query sees the 4096 keys before it).
   * chunk (sub-object ``chunk_prefill``): the last 2048-token chunk of an 8192-token GQA prompt
     (B=1, Hq=64, Hkv=8, D=128) against the 6144 tokens already in the KV cache; one
     attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
@@ -95,7 +97,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "swa", "all"], default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -135,9 +137,11 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
     torch.cuda.synchronize()
     flops = wl.prefill_flops()
 
+    W = wl.window if wl.window >= 0 else None
+
     def step():
         lib.rotate_keys_f16(k, tab, out=krot)
-        lib.prefill_prerotated(q, krot, v, tab, out=out)
+        lib.prefill_prerotated(q, krot, v, tab, window=W, out=out)
 
     log(f"[bench] timing {wl.name} prefill step: warmup {warmup}, steps {steps}")
     for _ in range(warmup):
@@ -152,7 +156,7 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
         a.record(stream)
         lib.rotate_keys_f16(k, tab, out=krot)
         b.record(stream)
-        lib.prefill_prerotated(q, krot, v, tab, out=out)
+        lib.prefill_prerotated(q, krot, v, tab, window=W, out=out)
         c.record(stream)
     end.record(stream)
     torch.cuda.synchronize()
@@ -189,7 +193,8 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     # One step is one attn_decode call; the steps are timed as a whole, without events between
     # them.  A decode step is ~0.16 ms, so it runs 4x the prefill step count (the clock settles
     # after the idle gap at the synchronize that opens the timed region).
-    ms = time_calls(lambda: lib.decode(q, kc, vc, cl, qp, tab, out=out, workspace=ws), steps, warmup)
+    W = wl.window if wl.window >= 0 else None
+    ms = time_calls(lambda: lib.decode(q, kc, vc, cl, qp, tab, window=W, out=out, workspace=ws), steps, warmup)
     nbytes = wl.decode_kv_bytes()
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
@@ -321,6 +326,10 @@ def main():
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only == "all":
         res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False)
+    if args.only in ("swa", "all"):
+        res["swa"] = bench_prefill(lib, inputs, W["swa"], max(5, args.steps // 2), max(3, args.warmup // 2),
+                                   variants=False)
+        res["swa_decode"] = bench_decode(lib, inputs, W["swa_decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("paged", "all"):
         res["paged"] = bench_paged_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("chunk", "all"):
@@ -394,6 +403,25 @@ def main():
             "attention_kernel_frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
                        "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale}}
+    if "swa" in res:
+        r = res["swa"]
+        wl = r["p"].wl
+        out["swa_prefill"] = {
+            "value": round(r["tflops_step"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_step"], 4),
+            "frac": round(r["tflops_step"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "attention_kernel_tflops": round(r["tflops_kernel"], 2),
+            "config": {"workload": "causal GQA prefill with a sliding window", "B": wl.B, "Hq": wl.Hq,
+                       "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D, "window": wl.window,
+                       "flops_per_step": wl.prefill_flops()}}
+    if "swa_decode" in res:
+        r = res["swa_decode"]
+        wl = r["d"].wl
+        out["swa_decode"] = {
+            "value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 5),
+            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4),
+            "config": {"workload": "batch decode with a sliding window", "B": wl.B, "cache_len": wl.S, "Hq": wl.Hq,
+                       "Hkv": wl.Hkv, "head_dim": wl.D, "window": wl.window,
+                       "kv_bytes_per_step": wl.decode_kv_bytes()}}
     if "paged" in res:
         r = res["paged"]
         wl = r["wl"]

@@ -32,6 +32,11 @@
  *   - Every argument that can be checked on the host is checked before any HIP call; a
  *     rejected call enqueues nothing.  HIP launch errors map to ATTN_ERR_HIP.
  *   - No C++ exception crosses this interface.  Calls are thread-safe (no shared state).
+ *   - window (every attention entry point): a negative value means no window.  window = W >= 0
+ *     is a sliding window ("Building Self-Attention and Transformer Engines",
+ *     codingpancake.com, section 6.4: each token attends only to the W tokens before it): the
+ *     query at position p sees only the keys at positions p - W .. p.  It requires the causal
+ *     mask.  W = 4096 is the page's example.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
@@ -102,6 +107,7 @@ attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int 
  *      pos0 + S <= table_max_pos.
  * causal != 0 masks key j > query i (square mask anchored at the top-left); causal == 0
  *      lets every query see every key.
+ * window: see the conventions above; W >= 0 also masks key j < i - W (needs causal != 0).
  * Scale: 1/sqrt(D), fixed.
  * workspace: optional device scratch of at least attn_prefill_workspace_bytes(B, Hkv, S, D)
  *      bytes (contents on entry irrelevant, overwritten).  Used only for bf16 input with RoPE:
@@ -116,13 +122,13 @@ attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int 
  * multiplied exactly.  The softmax weights are rounded to bf16 for the P.V product (fp32
  * accumulation).
  * Errors: ATTN_ERR_INVALID_ARG for null q/k/v/o, B/Hq/Hkv/S < 1, Hq % Hkv != 0, bad RoPE
- * range, a workspace that is misaligned or too small, misalignment; ATTN_ERR_UNSUPPORTED
- * outside the support matrix.
+ * range, a window without the causal mask, a workspace that is misaligned or too small,
+ * misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
  * --------------------------------------------------------------------------------------- */
 size_t attn_prefill_workspace_bytes(int B, int Hkv, int S, int D);
 attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                          attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
-                         int causal, int pos0, const float* rope_table, int table_max_pos,
+                         int causal, int pos0, int window, const float* rope_table, int table_max_pos,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
@@ -140,7 +146,7 @@ attn_status attn_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int
                                  const float* rope_table, int table_max_pos, void* stream);
 attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void* v, void* o,
                                     float* lse, attn_dtype out_dt, int B, int Hq, int Hkv, int S,
-                                    int D, int causal, int pos0, const float* rope_table,
+                                    int D, int causal, int pos0, int window, const float* rope_table,
                                     int table_max_pos, void* stream);
 
 /* ---------------------------------------------------------------------------------------
@@ -157,7 +163,8 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
  *   position s, computed in float32 and rounded to bf16 (nearest even); value rows copied.
  *   Other cache rows are not modified.
  * Step 2: o[b, h, i] = softmax over keys j <= pos0 + i of the cache rows [0, pos0 + Sq)
- *   (the causal mask aligned at the bottom right), the query rotated at position pos0 + i.
+ *   (the causal mask aligned at the bottom right), the query rotated at position pos0 + i;
+ *   with a window W >= 0 only keys j >= pos0 + i - W.
  *   Query head h reads KV head h / (Hq / Hkv).  Scale 1/sqrt(D).
  * o: [B, Hq, Sq, D] of dtype out_dt; lse: optional float32 [B, Hq, Sq] (natural log).
  * rope_table: NULL disables RoPE (keys copied into the cache as given, Q.K^T on the exact
@@ -174,9 +181,9 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
  * --------------------------------------------------------------------------------------- */
 attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                void* v_cache, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
-                               int Hkv, int Sq, int S_max, int D, int pos0, const float* rope_table,
-                               int table_max_pos, void* workspace, size_t workspace_bytes,
-                               void* stream);
+                               int Hkv, int Sq, int S_max, int D, int pos0, int window,
+                               const float* rope_table, int table_max_pos, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV
@@ -188,21 +195,25 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
  * [0, min(cache_len[b], S_max)); its query is rotated at position q_pos[b] (if rope_table
  * is not NULL).  A row with cache_len[b] <= 0 yields o = 0 and lse = -inf.  A row whose
  * q_pos[b] lies outside [0, table_max_pos) yields NaN (the table has no such row).
+ * Cache row j holds the token at position j; with a window W >= 0 only rows
+ * j >= q_pos[b] - W are read and seen (q_pos is then required; a row with none left yields
+ * o = 0 and lse = -inf).  Rows before the window are never used.
  * o: [B, Hq, 1, D] of dtype out_dt; lse: optional float32 [B, Hq].
  * n_split: number of cache chunks per (sequence, KV head); 0 picks one from the shape.
  * workspace: device scratch of at least attn_decode_workspace_bytes(...) bytes with the
  * same B, Hq, Hkv, S_max, D and n_split; its contents on entry do not matter.
  *
  * Support matrix: in_dt = ATTN_BF16, D in {64, 128}, out_dt either.
- * Errors: ATTN_ERR_INVALID_ARG for null pointers, sizes < 1, Hq % Hkv != 0, n_split < 0,
- * workspace too small, misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
+ * Errors: ATTN_ERR_INVALID_ARG for null pointers (q_pos may be NULL only without RoPE and
+ * without a window), sizes < 1, Hq % Hkv != 0, n_split < 0, workspace too small, misalignment;
+ * ATTN_ERR_UNSUPPORTED outside the support matrix.
  * --------------------------------------------------------------------------------------- */
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D, int n_split);
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split);
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
-                        int D, const float* rope_table, int table_max_pos, int n_split,
+                        int D, int window, const float* rope_table, int table_max_pos, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
@@ -217,8 +228,9 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
  *   blocks holding tokens [0, cache_len[b]) are read; the rest may hold anything.  An entry
  *   read outside [0, num_blocks) is clamped into it (no out-of-range access; the result is
  *   then meaningless).
- * cache_len, q_pos, q, o, lse, n_split, rope_table: as in attn_decode, with
- *   S_max = max_blocks * block_size (cache_len is clamped to it).
+ * cache_len, q_pos, q, o, lse, n_split, window, rope_table: as in attn_decode, with
+ *   S_max = max_blocks * block_size (cache_len is clamped to it).  With a window, blocks that
+ *   lie wholly before the window are not read (their table entries may be stale).
  * workspace: at least attn_decode_workspace_bytes(B, Hq, Hkv, max_blocks * block_size, D,
  *   n_split) bytes.
  * Support matrix: as attn_decode; block_size a power of two in [16, 4096].
@@ -229,8 +241,8 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
                               int block_size, const int32_t* block_table, int max_blocks,
                               const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
                               attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int D,
-                              const float* rope_table, int table_max_pos, int n_split, void* workspace,
-                              size_t workspace_bytes, void* stream);
+                              int window, const float* rope_table, int table_max_pos, int n_split,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -51,11 +51,11 @@ def test_rope_table_bytes():
 
 def _prefill(**kw):
     a = dict(q=A, k=A, v=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=1, Hq=8, Hkv=2, S=100, D=128,
-             causal=1, pos0=0, table=A, tmax=100, ws=None, wsb=0, stream=None)
+             causal=1, pos0=0, window=-1, table=A, tmax=100, ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.raw().attn_prefill(a["q"], a["k"], a["v"], a["o"], a["lse"], a["in_dt"], a["out_dt"], a["B"],
-                                  a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["pos0"], a["table"],
-                                  a["tmax"], a["ws"], a["wsb"], a["stream"])
+                                  a["Hq"], a["Hkv"], a["S"], a["D"], a["causal"], a["pos0"], a["window"],
+                                  a["table"], a["tmax"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -67,6 +67,7 @@ def _prefill(**kw):
     (dict(D=96), UNSUP), (dict(D=32), UNSUP), (dict(D=256), UNSUP), (dict(in_dt=F32, out_dt=BF16), UNSUP),
     (dict(D=96, table=None), UNSUP),
     (dict(ws=A, wsb=2 * 100 * 128 * 2 - 1), INV), (dict(ws=MIS, wsb=1 << 20), INV),
+    (dict(causal=0, window=10), INV), (dict(causal=0, window=0), INV),
 ])
 def test_prefill_rejects(kw, code):
     assert _prefill(**kw) == code
@@ -74,14 +75,14 @@ def test_prefill_rejects(kw, code):
 
 def _decode(**kw):
     a = dict(q=A, kc=A, vc=A, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=4, Hq=16, Hkv=2,
-             S=1000, D=128, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
+             S=1000, D=128, window=-1, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = lib.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], max(a["S"], 1), max(a["D"], 1),
                                               max(a["ns"], 0))
     return lib.raw().attn_decode(a["q"], a["kc"], a["vc"], a["cl"], a["qp"], a["o"], a["lse"], a["in_dt"],
-                                 a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["table"], a["tmax"],
-                                 a["ns"], a["ws"], a["wsb"], a["stream"])
+                                 a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["window"], a["table"],
+                                 a["tmax"], a["ns"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -91,6 +92,7 @@ def _decode(**kw):
     (dict(wsb=16), INV), (dict(kc=MIS), INV), (dict(ws=MIS), INV), (dict(cl=P(0x10002)), INV),
     (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
     (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+    (dict(table=None, qp=None, window=100), INV),           # a window needs the query positions
 ])
 def test_decode_rejects(kw, code):
     assert _decode(**kw) == code
@@ -120,9 +122,10 @@ def test_two_stage_prefill_rejects():
     assert rot(out=MIS) == INV
     assert rot(D=96) == UNSUP
     pre = lambda q=A, k=A, v=A, o=A, lse=None, odt=BF16, B=1, Hq=4, Hkv=2, S=10, D=128, causal=1, pos0=0, \
-        table=A, tmax=10: raw.attn_prefill_prerotated(q, k, v, o, lse, odt, B, Hq, Hkv, S, D, causal, pos0,
-                                                      table, tmax, None)
+        window=-1, table=A, tmax=10: raw.attn_prefill_prerotated(q, k, v, o, lse, odt, B, Hq, Hkv, S, D, causal,
+                                                                 pos0, window, table, tmax, None)
     assert pre(table=None) == INV
+    assert pre(causal=0, window=3) == INV
     assert pre(Hkv=3) == INV
     assert pre(k=MIS) == INV
     assert pre(odt=5) == INV
@@ -161,13 +164,13 @@ def test_decode_workspace_geometry():
 
 def _chunk(**kw):
     a = dict(q=A, kn=A, vn=A, kc=A, vc=A, o=A, lse=None, out_dt=BF16, B=2, Hq=8, Hkv=2, Sq=100, S_max=300,
-             D=128, pos0=50, table=A, tmax=300, ws=A, wsb=None, stream=None)
+             D=128, pos0=50, window=-1, table=A, tmax=300, ws=A, wsb=None, stream=None)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = 2 * 2 * (50 + 100) * 128 * 2
     return lib.raw().attn_prefill_chunk(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["o"], a["lse"], a["out_dt"],
                                         a["B"], a["Hq"], a["Hkv"], a["Sq"], a["S_max"], a["D"], a["pos0"],
-                                        a["table"], a["tmax"], a["ws"], a["wsb"], a["stream"])
+                                        a["window"], a["table"], a["tmax"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -188,14 +191,15 @@ def test_prefill_chunk_rejects(kw, code):
 
 def _paged(**kw):
     a = dict(q=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=64, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16,
-             B=4, Hq=16, Hkv=2, D=128, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
+             B=4, Hq=16, Hkv=2, D=128, window=-1, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)
     a.update(kw)
     if a["wsb"] is None:
         a["wsb"] = lib.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], max(a["mb"] * a["bs"], 1),
                                               max(a["D"], 1), max(a["ns"], 0))
     return lib.raw().attn_decode_paged(a["q"], a["kp"], a["vp"], a["nblk"], a["bs"], a["bt"], a["mb"], a["cl"],
                                        a["qp"], a["o"], a["lse"], a["in_dt"], a["out_dt"], a["B"], a["Hq"], a["Hkv"],
-                                       a["D"], a["table"], a["tmax"], a["ns"], a["ws"], a["wsb"], a["stream"])
+                                       a["D"], a["window"], a["table"], a["tmax"], a["ns"], a["ws"], a["wsb"],
+                                       a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -206,6 +210,7 @@ def _paged(**kw):
     (dict(wsb=16), INV), (dict(kp=MIS), INV), (dict(ws=MIS), INV), (dict(bt=P(0x10002)), INV),
     (dict(cl=P(0x10002)), INV), (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
     (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+    (dict(table=None, qp=None, window=0), INV),
 ])
 def test_decode_paged_rejects(kw, code):
     assert _paged(**kw) == code

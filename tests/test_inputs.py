@@ -119,3 +119,19 @@ def test_paged_decode_layout():
     # same draws as the contiguous generator
     d2 = inputs.make_decode(wl)
     assert np.array_equal(d.k_cache.bits, d2.k_cache.bits) and np.array_equal(d.q.bits, d2.q.bits)
+
+
+def test_window_work_counts():
+    import dataclasses
+    swa = inputs.WORKLOADS["swa"]
+    S, W = 32768, 4096
+    assert swa.prefill_flops() == 4 * 32 * 128 * (S * S / 2 - (S - W - 1) * (S - W) / 2)
+    # a window covering every key counts like plain causal
+    assert dataclasses.replace(swa, window=S - 1).prefill_flops() == 2 * 32 * S * S * 128
+    assert dataclasses.replace(swa, window=-1).prefill_flops() == 2 * 32 * S * S * 128
+    # brute count of visible pairs (i - W <= j <= i) on a small case matches within the diagonal convention
+    s, w = 50, 7
+    pairs = sum(1 for i in range(s) for j in range(s) if i - w <= j <= i)
+    small = dataclasses.replace(swa, S=s, window=w, B=1, Hq=1, D=1)
+    assert abs(small.prefill_flops() / 4 - pairs) <= s / 2     # S^2/2 convention vs S(S+1)/2 exact
+    assert inputs.WORKLOADS["swa_decode"].decode_kv_bytes() == (1 << 30) // 2

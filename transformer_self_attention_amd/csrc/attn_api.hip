@@ -19,6 +19,10 @@ inline attn_status from_hip(hipError_t e) { return e == hipSuccess ? ATTN_OK : A
 
 inline bool valid_dtype(attn_dtype d) { return d == ATTN_F32 || d == ATTN_BF16; }
 
+// window < 0: none; window >= 0: W keys before each query (causal attention only).
+inline bool valid_window(int window, bool causal) { return window < 0 || causal; }
+inline int kernel_window(int window) { return window < 0 || window >= attn::kNoWindow ? attn::kNoWindow : window; }
+
 attn_status check_rope(const float* table, int table_max_pos, int pos0, int S) {
   if (!table) return ATTN_OK;
   if (!aligned16(table) || table_max_pos < 1 || pos0 < 0) return ATTN_ERR_INVALID_ARG;
@@ -98,13 +102,14 @@ size_t attn_prefill_workspace_bytes(int B, int Hkv, int S, int D) {
 
 attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, float* lse,
                          attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D,
-                         int causal, int pos0, const float* rope_table, int table_max_pos,
+                         int causal, int pos0, int window, const float* rope_table, int table_max_pos,
                          void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k || !v || !o) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
   if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!valid_window(window, causal != 0)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_INVALID_ARG;
   if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
@@ -120,6 +125,7 @@ attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, f
   a.out_bf16 = out_dt == ATTN_BF16;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
   a.Sk = S; a.k_rows = S; a.v_rows = S; a.coff = 0;
+  a.window = kernel_window(window);
   a.causal = causal != 0;
   a.pos0 = pos0;
   a.table = rope_table;
@@ -140,11 +146,13 @@ attn_status attn_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int
 
 attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void* v, void* o, float* lse,
                                     attn_dtype out_dt, int B, int Hq, int Hkv, int S, int D, int causal,
-                                    int pos0, const float* rope_table, int table_max_pos, void* stream) {
+                                    int pos0, int window, const float* rope_table, int table_max_pos,
+                                    void* stream) {
   if (!q || !k_rot || !v || !o || !rope_table) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || (D & 1)) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_window(window, causal != 0)) return ATTN_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k_rot) || !aligned16(v) || !aligned16(o) || (lse && !aligned16(lse)))
     return ATTN_ERR_INVALID_ARG;
   if (check_rope(rope_table, table_max_pos, pos0, S) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
@@ -155,6 +163,7 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
   a.out_bf16 = out_dt == ATTN_BF16;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = S; a.D = D;
   a.Sk = S; a.k_rows = S; a.v_rows = S; a.coff = 0;
+  a.window = kernel_window(window);
   a.causal = causal != 0;
   a.pos0 = pos0;
   a.table = rope_table;
@@ -164,9 +173,9 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
 
 attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_new, void* k_cache,
                                void* v_cache, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
-                               int Hkv, int Sq, int S_max, int D, int pos0, const float* rope_table,
-                               int table_max_pos, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+                               int Hkv, int Sq, int S_max, int D, int pos0, int window,
+                               const float* rope_table, int table_max_pos, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !o) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || S_max < 1 || D < 1 || pos0 < 0) return ATTN_ERR_INVALID_ARG;
@@ -186,8 +195,11 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
 
   hipStream_t st = (hipStream_t)stream;
   void* k16 = rope_table ? workspace : nullptr;
+  const int kw = kernel_window(window);
+  // key rows the attention can still read: from the 64-key tile holding the first row's window start
+  const int conv_first = kw >= pos0 ? 0 : ((pos0 - kw) / 64) * 64;
   const hipError_t e = attn::launch_cache_append(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max,
-                                                 D, pos0, rope_table, st);
+                                                 D, pos0, conv_first, rope_table, st);
   if (e != hipSuccess) return ATTN_ERR_HIP;
   attn::PrefillArgs a;
   a.q = q; a.k = rope_table ? k16 : k_cache; a.v = v_cache; a.o = o; a.lse = lse;
@@ -198,6 +210,7 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
   a.table = rope_table;
   a.workspace = nullptr;
   a.Sk = Sk; a.k_rows = rope_table ? Sk : S_max; a.v_rows = S_max; a.coff = pos0;
+  a.window = kw;
   return from_hip(attn::launch_prefill_cache(a, st));
 }
 
@@ -220,10 +233,10 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D, int
 attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
-                        int D, const float* rope_table, int table_max_pos, int n_split,
+                        int D, int window, const float* rope_table, int table_max_pos, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream) {
   if (!q || !k_cache || !v_cache || !cache_len || !o || !workspace) return ATTN_ERR_INVALID_ARG;
-  if (rope_table && !q_pos) return ATTN_ERR_INVALID_ARG;
+  if ((rope_table || window >= 0) && !q_pos) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return ATTN_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
@@ -255,17 +268,18 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
   a.ws_ml = static_cast<float*>(workspace) + parts * D;
   a.block_table = nullptr;
   a.max_blocks = 0; a.bs_log2 = 0; a.num_blocks = 0;
+  a.window = kernel_window(window);
   return from_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 
 attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int num_blocks,
                               int block_size, const int32_t* block_table, int max_blocks,
                               const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
-                              attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int D,
+                              attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int D, int window,
                               const float* rope_table, int table_max_pos, int n_split, void* workspace,
                               size_t workspace_bytes, void* stream) {
   if (!q || !k_pages || !v_pages || !block_table || !cache_len || !o || !workspace) return ATTN_ERR_INVALID_ARG;
-  if (rope_table && !q_pos) return ATTN_ERR_INVALID_ARG;
+  if ((rope_table || window >= 0) && !q_pos) return ATTN_ERR_INVALID_ARG;
   if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
   if (B < 1 || Hq < 1 || Hkv < 1 || D < 1 || num_blocks < 1 || max_blocks < 1 || n_split < 0)
     return ATTN_ERR_INVALID_ARG;
@@ -304,6 +318,7 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
   while ((1 << lg) < block_size) ++lg;
   a.bs_log2 = lg;
   a.num_blocks = num_blocks;
+  a.window = kernel_window(window);
   return from_hip(attn::launch_decode(a, (hipStream_t)stream));
 }
 

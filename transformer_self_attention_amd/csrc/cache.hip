@@ -24,10 +24,11 @@ template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint16_t* __restrict__ k16,
-    int64_t n_bh, int Sq, int S_max, int pos0, const float2* __restrict__ table) {
+    int64_t n_bh, int Sq, int S_max, int pos0, int conv_first, const float2* __restrict__ table) {
   constexpr int NCH = D / 8;  // 16-byte chunks per row
-  // rows handled per (batch, KV head): [first, pos0 + Sq)
-  const int first = ROPE ? 0 : pos0;
+  // rows handled per (batch, KV head): [first, pos0 + Sq); with RoPE the earlier rows from
+  // conv_first on (those a sliding window can still see) are converted to fp16
+  const int first = ROPE ? conv_first : pos0;
   const int Sk = pos0 + Sq;
   const int nrows = Sk - first;
   const int64_t n = n_bh * nrows * NCH;
@@ -73,9 +74,10 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
 
 template <int D>
 hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* k16,
-                     int B, int Hkv, int Sq, int S_max, int pos0, const float* table, hipStream_t st) {
+                     int B, int Hkv, int Sq, int S_max, int pos0, int conv_first, const float* table,
+                     hipStream_t st) {
   const int64_t n_bh = (int64_t)B * Hkv;
-  const int64_t rows = table ? (int64_t)(pos0 + Sq) : (int64_t)Sq;
+  const int64_t rows = table ? (int64_t)(pos0 + Sq - conv_first) : (int64_t)Sq;
   const int64_t n = n_bh * rows * (D / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 workgroups per CU
@@ -83,12 +85,12 @@ hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* 
   if (table)
     hipLaunchKernelGGL((cache_append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, (uint16_t*)k16, n_bh, Sq, S_max, pos0,
+                       (uint16_t*)v_cache, (uint16_t*)k16, n_bh, Sq, S_max, pos0, conv_first,
                        reinterpret_cast<const float2*>(table));
   else
     hipLaunchKernelGGL((cache_append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, (uint16_t*)nullptr, n_bh, Sq, S_max, pos0,
+                       (uint16_t*)v_cache, (uint16_t*)nullptr, n_bh, Sq, S_max, pos0, pos0,
                        (const float2*)nullptr);
   return hipGetLastError();
 }
@@ -97,9 +99,11 @@ hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* 
 
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
-                               const float* table, hipStream_t st) {
-  return D == 64 ? append_go<64>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, table, st)
-                 : append_go<128>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, table, st);
+                               int conv_first, const float* table, hipStream_t st) {
+  return D == 64 ? append_go<64>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
+                                 table, st)
+                 : append_go<128>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
+                                  table, st);
 }
 
 }  // namespace attn

@@ -76,6 +76,8 @@ struct PrefillArgs {
   // Keys: Sk rows per (batch, KV head), stored k_rows / v_rows rows apart (K / V); query row i
   // sees key j when j <= i + coff.  An ordinary prefill has Sk = k_rows = v_rows = S, coff = 0.
   int Sk, k_rows, v_rows, coff;
+  // Sliding window: key j is visible to row i only if j >= i + coff - window (no window: 1 << 30).
+  int window;
 };
 
 size_t prefill_workspace_bytes(int B, int Hkv, int S, int D);
@@ -86,11 +88,12 @@ hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, in
 hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st);
 
 // Chunked prefill against a KV cache (bf16): append the chunk's keys (rotated, rounded to bf16)
-// and values to cache rows [pos0, pos0 + Sq); with RoPE also write every key row [0, pos0 + Sq)
-// as fp16 into k16 ([B*Hkv, pos0 + Sq, D]), the operand format of the Q.K^T product.
+// and values to cache rows [pos0, pos0 + Sq); with RoPE also write key rows [conv_first,
+// pos0 + Sq) as fp16 into k16 ([B*Hkv, pos0 + Sq, D]), the operand format of the Q.K^T product
+// (rows before conv_first are never read: a sliding window no longer reaches them).
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
-                               const float* table, hipStream_t st);
+                               int conv_first, const float* table, hipStream_t st);
 // The attention of a chunk against the cache: a.k holds the fp16 keys (a.table != nullptr) or
 // the bf16 cache keys (no RoPE).
 hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st);
@@ -116,7 +119,11 @@ struct DecodeArgs {
   // S_max = max_blocks << bs_log2.
   const int32_t* block_table;
   int max_blocks, bs_log2, num_blocks;
+  // Sliding window: cache row j is visible only if j >= q_pos[b] - window (no window: 1 << 30).
+  int window;
 };
+
+constexpr int kNoWindow = 1 << 30;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
 

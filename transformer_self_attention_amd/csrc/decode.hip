@@ -31,6 +31,11 @@
 // sub-block lies in one block: the two block ids are wave-uniform scalars, fetched one sub-block
 // ahead of the loads that use them, and every lane's K/V address is the block's base plus its
 // slot, exactly as in the contiguous cache.
+//
+// Sliding window (codingpancake.com section 6.4): only cache rows j >= q_pos[b] - window are
+// visible.  Each split starts at the first 32-key sub-block holding a visible row; the rows
+// before the window in that sub-block are masked, and their values are never used (zeroed), so
+// blocks before the window may already have been released and reused.
 #include "common.h"
 
 namespace attn {
@@ -73,7 +78,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int Hq, int Hkv,
     int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse,
-    const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks) {
+    const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks, int window) {
   constexpr int kWaves = NW;
   constexpr int kThreads = NW * 64;
   constexpr int NCH = D / 8;
@@ -95,8 +100,13 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 
   int L = cache_len[b];
   L = L < 0 ? 0 : (L > S_max ? S_max : L);
-  const int kbeg = split * chunk;
-  const int kend = min(kbeg + chunk, L);
+  // first visible row (sliding window); q_pos is given whenever a window is
+  const int wstart = window < kNoWindow ? max(q_pos[b] - window, 0) : 0;
+  const int kbeg = max(split * chunk, wstart & ~(kSub - 1));
+  const int kend0 = min(split * chunk + chunk, L);
+  // nothing visible in this split: empty range (then every sub-block processed below holds at
+  // least one visible row, the first one holding wstart)
+  const int kend = wstart < kend0 ? kend0 : 0;
 
   // ---- query fragments (hi/lo bf16), rotated at q_pos[b] and scaled by log2(e)/sqrt(D) ----
   bf16x8 qhi[KS], qlo[KS];
@@ -172,7 +182,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int key = k0 + kb * 16 + i16;
-      const bool ok = key < kend;
+      const bool ok = key < kend && key >= wstart;
       int64_t row;
       if constexpr (PAGED) row = ok ? (kb ? r1 : r0) + i16 : r0;
       else row = ok ? key : kbeg;
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     for (int i = 0; i < LPT; ++i) {
       const int c = lane + 64 * i;
       const int key = k0 + c / NCH;
-      const bool ok = key < kend;
+      const bool ok = key < kend && key >= wstart;
       int64_t row;
       if constexpr (PAGED) row = ok ? ((c / NCH) >= 16 ? r1 : r0) + ((c / NCH) & 15) : r0;
       else row = ok ? key : kbeg;
@@ -239,12 +249,14 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         sacc[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qlo[ks], sacc[kb], 0, 0, 0);
       }
     }
-    if (k0 + kSub > kend) {
+    if (k0 + kSub > kend || k0 < wstart) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (k0 + kb * 16 + 4 * g16 + r >= kend) sacc[kb][r] = -INFINITY;
+        for (int r = 0; r < 4; ++r) {
+          const int key = k0 + kb * 16 + 4 * g16 + r;
+          if (key >= kend || key < wstart) sacc[kb][r] = -INFINITY;
+        }
     }
     float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                      fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
@@ -379,18 +391,18 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED>), dim3(1, a.Hkv, a.B),
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
-                         a.max_blocks, a.bs_log2, a.num_blocks);
+                         a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     else
       hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED>), dim3(1, a.Hkv, a.B),
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
-                         a.max_blocks, a.bs_log2, a.num_blocks);
+                         a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     return hipGetLastError();
   }
   hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED>),
                      dim3(a.n_split, a.Hkv, a.B), dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
                      a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse,
-                     a.block_table, a.max_blocks, a.bs_log2, a.num_blocks);
+                     a.block_table, a.max_blocks, a.bs_log2, a.num_blocks, a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (a.out_bf16)

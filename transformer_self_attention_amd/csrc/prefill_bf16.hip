@@ -31,6 +31,9 @@
 //  * Causal: tiles entirely above a wave's rows are skipped; only tiles crossing the diagonal (or
 //    the tail of the keys) are masked.  The diagonal may be shifted by coff keys: a chunk of
 //    queries at the end of a longer key sequence (a KV cache) sees every earlier key.
+//  * Sliding window (codingpancake.com section 6.4): a query sees only the `window` keys before
+//    it (and itself); tiles entirely before a wave's windows are skipped, and the workgroup
+//    starts at the first tile any of its rows can see.
 //  * Workgroup order: heaviest query blocks first; the G query heads sharing one KV head (and the
 //    same query block) go to the same XCD so its L2 serves their K/V reads.
 #include "common.h"
@@ -61,12 +64,13 @@ __device__ __forceinline__ int swz(int r, int lc) {
   }
 }
 
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW>
+// WIN: a sliding window is applied (causal only); without it the window code is compiled out.
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW, bool WIN>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 2, NW / 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Sk,
-                         int k_rows, int v_rows, int coff, int pos0,
+                         int k_rows, int v_rows, int coff, int window, int pos0,
                          const float2* __restrict__ table) {
   constexpr int NT = NW * 64;                // threads per workgroup
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
@@ -150,11 +154,13 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 
   // ---- key range ----
-  // Query row i sees key j when j <= i + coff (coff = 0: the square mask; coff = Sk - Sq: the
-  // mask aligned at the bottom right, for a chunk of queries at the end of the keys).
+  // Query row i sees key j when i + coff - window <= j <= i + coff (coff = 0: the square mask;
+  // coff = Sk - Sq: the mask aligned at the bottom right, for a chunk of queries at the end of
+  // the keys; window >= 2^30: no window).
   const int q_last = min(q0 + BM, Sq) - 1;
   const int key_end = CAUSAL ? min(q_last + 1 + coff, Sk) : Sk;
   const int n_tiles = (key_end + kBN - 1) / kBN;
+  const int t_first = (CAUSAL && WIN) ? max(0, q0 + coff - window) / kBN : 0;
   const uint16_t* kg = k + ((int64_t)b * Hkv + hkv) * k_rows * D;
   const uint16_t* vg = v + ((int64_t)b * Hkv + hkv) * v_rows * D;
   // HBM -> LDS with no register staging: wave-load i of this wave fills LDS chunks
@@ -296,7 +302,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     __syncthreads();
     if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
 
-    if (!CAUSAL || k0 <= qw + kRowsPerWave - 1 + coff) {
+    if (!CAUSAL || (k0 <= qw + kRowsPerWave - 1 + coff && (!WIN || k0 + kBN - 1 >= qw + coff - window))) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
       const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
       // S^T = K Q^T for two 32-key blocks
@@ -324,14 +330,17 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           for (int r = 0; r < 16; ++r) sacc[kb][r] *= c_log2;
       }
       // mask (diagonal / tail tiles only)
-      const bool need_mask = (CAUSAL && k0 + kBN - 1 > qw + coff) || (k0 + kBN > Sk);
+      const bool need_mask =
+          (CAUSAL && (k0 + kBN - 1 > qw + coff || (WIN && k0 < qw + kRowsPerWave - 1 + coff - window))) ||
+          (k0 + kBN > Sk);
       if (need_mask) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if ((CAUSAL && key > row + coff) || key >= Sk) sacc[kb][r] = -INFINITY;
+            if ((CAUSAL && (key > row + coff || (WIN && key < row + coff - window))) || key >= Sk)
+              sacc[kb][r] = -INFINITY;
           }
       }
       bf16x8 pf[2][2];
@@ -372,8 +381,10 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         if (__builtin_amdgcn_ballot_w64(m_run == -INFINITY || !(lsum <= kWeightSumBound)) != 0) {
           const float mx = tile_max();
           const float m_new = m_run == -INFINITY ? mx : m_run + fmaxf(mx, 0.f);
-          const float alpha = fast_exp2(m_run - m_new);   // 0 while m_run is -inf
-          const float shift = m_new + s_init;             // subtract to put sacc on m_new's scale
+          // none: the row has seen no key yet (only with a sliding window); it stays at -inf
+          const bool none = WIN && m_new == -INFINITY;
+          const float alpha = none ? 1.f : fast_exp2(m_run - m_new);   // 0 while m_run is -inf
+          const float shift = none ? 0.f : m_new + s_init;   // subtract to put sacc on m_new's scale
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
@@ -384,7 +395,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
             for (int r = 0; r < 16; ++r) sacc[kb][r] -= shift;
           m_run = m_new;
-          s_init = -m_new;
+          s_init = none ? 0.f : -m_new;
 #pragma unroll
           for (int r = 0; r < 16; ++r) s_init_v[r] = s_init;
           weights();
@@ -394,7 +405,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         const float m_new = fmaxf(m_run, mx);
         const bool need = m_new > m_run + kRescaleThreshold;
         if (__builtin_amdgcn_ballot_w64(need) != 0) {
-          const float alpha = fast_exp2(m_run - m_new);
+          // a row that still sees no key (sliding window) keeps m = -inf and needs no rescale
+          const float alpha = (WIN && m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
           l_run *= alpha;
 #pragma unroll
           for (int db = 0; db < DB; ++db)
@@ -403,7 +415,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           m_run = m_new;
         }
         // p = 2^(s - m), packed to bf16 as the B operand of P.V; the row sum adds the same
-        // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1))
+        // rounded weights, two at a time (v_dot2_f32_bf16 against (1, 1)).  A row that has seen
+        // no key yet (sliding window) has m = -inf and only -inf scores: its weights are 0.
+        const float m_sub = (WIN && m_run == -INFINITY) ? 0.f : m_run;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -411,8 +425,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 #pragma unroll
             for (int tt = 0; tt < 8; tt += 2) {
               bf16x2 pp;
-              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt] - m_run);
-              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1] - m_run);
+              pp[0] = (__bf16)fast_exp2(sacc[kb][8 * s + tt] - m_sub);
+              pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1] - m_sub);
               pf[kb][s][tt] = pp[0];
               pf[kb][s][tt + 1] = pp[1];
               lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
@@ -450,9 +464,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if (t + 1 < n_tiles) fused_issue(k0 + kBN);
   };
 
-  issue_tile(0, k_lds0, v_lds0);
-  fused_issue(0);
-  for (int t = 0; t < n_tiles; t += 2) {
+  issue_tile(t_first * kBN, k_lds0, v_lds0);
+  fused_issue(t_first * kBN);
+  for (int t = t_first; t < n_tiles; t += 2) {
     tile_step(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
   }
@@ -510,7 +524,7 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
   }
 }
 
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16>
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, bool WIN>
 hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   constexpr int NW = kWavesStream;
   constexpr int BM = NW * kRowsPerWave;
@@ -518,18 +532,21 @@ hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   const int nqb = (a.S + BM - 1) / BM;
   const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW, WIN>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.Sk, a.k_rows,
-                     a.v_rows, a.coff, a.pos0, reinterpret_cast<const float2*>(a.table));
+                     a.v_rows, a.coff, a.window, a.pos0, reinterpret_cast<const float2*>(a.table));
   return hipGetLastError();
 }
 
 template <int D, int KMODE>
 hipError_t dispatch_mode(const PrefillArgs& a, const void* kptr, hipStream_t st) {
-  if (a.causal)
-    return a.out_bf16 ? go<D, true, KMODE, true>(a, kptr, st) : go<D, true, KMODE, false>(a, kptr, st);
-  return a.out_bf16 ? go<D, false, KMODE, true>(a, kptr, st) : go<D, false, KMODE, false>(a, kptr, st);
+  if (a.causal) {
+    if (a.window < kNoWindow)
+      return a.out_bf16 ? go<D, true, KMODE, true, true>(a, kptr, st) : go<D, true, KMODE, false, true>(a, kptr, st);
+    return a.out_bf16 ? go<D, true, KMODE, true, false>(a, kptr, st) : go<D, true, KMODE, false, false>(a, kptr, st);
+  }
+  return a.out_bf16 ? go<D, false, KMODE, true, false>(a, kptr, st) : go<D, false, KMODE, false, false>(a, kptr, st);
 }
 
 template <int D>

@@ -5,7 +5,8 @@
 // the "Multi-Head Attention & Rotary Position Embeddings (RoPE)" listing (learnllm.online), RoPE
 // of devthesis section 3 applied to Q and K as their tiles are loaded, and the tiling with a
 // running max and sum of "Building Self-Attention and Transformer Engines" (codingpancake.com)
-// section 4.1.
+// section 4.1.  An optional sliding window (same page, section 6.4) limits each row to the
+// `window` keys before it.
 //
 // One wave (64 lanes) owns 32 query rows; lanes l and l+32 hold the two halves of row l's head
 // dimension, so the q and o vectors of a row live in registers and a dot product needs one
@@ -23,8 +24,8 @@ constexpr int kKeys = 32;  // keys per tile
 template <int D>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int S, int causal, int pos0,
-    const float2* __restrict__ table) {
+    float* __restrict__ o, float* __restrict__ lse, int Hq, int Hkv, int S, int causal, int window,
+    int pos0, const float2* __restrict__ table) {
   constexpr int H = D / 2;  // elements per lane
   __shared__ float ks[kKeys][D];
   __shared__ float vs[kKeys][D];
@@ -62,8 +63,12 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
   const float* vbase = v + ((int64_t)b * Hkv + kvh) * S * D;
   const int last_row = min(qb * kRows + kRows, S) - 1;
   const int key_end = causal ? last_row + 1 : S;
+  // visible keys of this row: [lo, hi] (causal: hi = row; sliding window: lo = row - window)
+  const int hi = causal ? row : S - 1;
+  const int lo = causal ? max(row - window, 0) : 0;
+  const int key_begin = causal ? (max(0, qb * kRows - window) / kKeys) * kKeys : 0;
 
-  for (int k0 = 0; k0 < key_end; k0 += kKeys) {
+  for (int k0 = key_begin; k0 < key_end; k0 += kKeys) {
     __syncthreads();
     // Stage 32 keys: each lane moves pairs (2 floats) at a time, rotating K.
     for (int e = lane; e < kKeys * D / 2; e += 64) {
@@ -92,9 +97,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
       float part = 0.f;
 #pragma unroll
       for (int d = 0; d < H; ++d) part = fmaf(qv[d], ks[j][half * H + d], part);
-      s[j] = (part + swap_halves(part)) * scale;
+      const float sj = (part + swap_halves(part)) * scale;
       const int key = k0 + j;
-      if (key >= S || (causal && key > row)) s[j] = -INFINITY;
+      s[j] = (key >= lo && key <= hi && key < S) ? sj : -INFINITY;
     }
     float m_tile = -INFINITY;
 #pragma unroll
@@ -133,11 +138,11 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
   if (a.D == 64)
     hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, dim3(64), 0, st, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Hq, a.Hkv, a.S,
-                       (int)a.causal, a.pos0, tab);
+                       (int)a.causal, a.window, a.pos0, tab);
   else
     hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, dim3(64), 0, st, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, a.Hq, a.Hkv, a.S,
-                       (int)a.causal, a.pos0, tab);
+                       (int)a.causal, a.window, a.pos0, tab);
   return hipGetLastError();
 }
 

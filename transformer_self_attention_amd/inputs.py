@@ -44,14 +44,19 @@ class Workload:
     rope_base: float = 10000.0
     pos0: int = 0            # chunk: position of the chunk's first token (cache rows before it are filled)
     S_max: int = 0           # chunk: cache rows per (sequence, KV head)
+    window: int = -1         # sliding window W (a query sees the W keys before it); -1: none
 
     @property
     def group(self) -> int:
         return self.Hq // self.Hkv
 
     def prefill_flops(self) -> float:
-        """Causal half of the two S x S x D contractions: 2*B*Hq*S^2*D."""
-        return 2.0 * self.B * self.Hq * self.S * self.S * self.D
+        """Causal half of the two S x S x D contractions: 2*B*Hq*S^2*D.  With a sliding window W
+        the (S-W-1)(S-W)/2 query-key pairs before the windows are not counted."""
+        pairs = self.S * self.S / 2.0
+        if 0 <= self.window < self.S - 1:
+            pairs -= (self.S - self.window - 1) * (self.S - self.window) / 2.0
+        return 4.0 * self.B * self.Hq * self.D * pairs
 
     def prefill_bytes(self) -> int:
         """Bytes a prefill must move at least: read Q, K and V once, write O once."""
@@ -65,9 +70,11 @@ class Workload:
         return 4.0 * self.B * self.Hq * self.D * (self.pos0 * self.S + self.S * self.S / 2.0)
 
     def decode_kv_bytes(self) -> int:
-        """K and V cache bytes one decode step must read."""
+        """K and V cache bytes one decode step must read (query at position S; with a sliding
+        window W only the last min(S, W) cache rows are visible)."""
         esz = 2 if self.dtype == "bf16" else 4
-        return 2 * self.B * self.Hkv * self.S * self.D * esz
+        rows = self.S if self.window < 0 else min(self.S, self.window)
+        return 2 * self.B * self.Hkv * rows * self.D * esz
 
 
 WORKLOADS = {
@@ -78,6 +85,11 @@ WORKLOADS = {
     "decode": Workload("decode", B=32, Hq=64, Hkv=8, S=8192, D=128, dtype="bf16", seed=3, kind="decode"),
     "long": Workload("long", B=1, Hq=32, Hkv=8, S=32768, D=128, dtype="bf16", seed=4, kind="prefill",
                      check_rows=128, big_key_frac=0.01, big_key_scale=8.0),
+    # the long-context prefill and the decode workload with a 4096-token sliding window
+    "swa": Workload("swa", B=1, Hq=32, Hkv=8, S=32768, D=128, dtype="bf16", seed=6, kind="prefill",
+                    check_rows=128, window=4096),
+    "swa_decode": Workload("swa_decode", B=32, Hq=64, Hkv=8, S=8192, D=128, dtype="bf16", seed=3, kind="decode",
+                           window=4096),
     # the last 2048-token chunk of an 8192-token GQA prompt, against the 6144 tokens already cached
     "chunk": Workload("chunk", B=1, Hq=64, Hkv=8, S=2048, D=128, dtype="bf16", seed=5, kind="chunk",
                       check_rows=128, pos0=6144, S_max=8192),

@@ -62,26 +62,26 @@ def _load():
     lib.attn_prefill_workspace_bytes.restype = sz
     lib.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32]
     lib.attn_prefill.restype = i32
-    lib.attn_prefill.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, i32,
+    lib.attn_prefill.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, i32, i32,
                                  fp, i32, vp, sz, vp]
     lib.attn_rotate_keys_f16.restype = i32
     lib.attn_rotate_keys_f16.argtypes = [vp, vp, i32, i32, i32, i32, i32, fp, i32, vp]
     lib.attn_prefill_prerotated.restype = i32
     lib.attn_prefill_prerotated.argtypes = [vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                            fp, i32, vp]
+                                            i32, fp, i32, vp]
     lib.attn_prefill_chunk.restype = i32
     lib.attn_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                       fp, i32, vp, sz, vp]
+                                       i32, fp, i32, vp, sz, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
     lib.attn_decode_num_splits.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode.restype = i32
-    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, fp,
+    lib.attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, fp,
                                 i32, i32, vp, sz, vp]
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
-                                      fp, i32, i32, vp, sz, vp]
+                                      i32, fp, i32, i32, vp, sz, vp]
     return lib
 
 
@@ -126,6 +126,15 @@ def _dt(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return ATTN_F32
     raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _win(window) -> int:
+    """Python's window=None (no window) as the ABI's negative value."""
+    if window is None:
+        return -1
+    if window < 0:
+        raise ValueError("window must be None or >= 0")
+    return int(window)
 
 
 def _need(t: torch.Tensor, name: str):
@@ -173,9 +182,11 @@ def prefill_workspace_bytes(B, Hkv, S, D) -> int:
     return int(_lib.attn_prefill_workspace_bytes(B, Hkv, S, D))
 
 
-def prefill(q, k, v, table=None, *, causal=True, pos0=0, out=None, out_dtype=None, lse=None,
+def prefill(q, k, v, table=None, *, causal=True, pos0=0, window=None, out=None, out_dtype=None, lse=None,
             workspace=None, stream=None):
     """o = softmax(rope(q) rope(k)^T / sqrt(D)) v over [B, H, S, D] tensors (GQA when Hkv < Hq).
+
+    window: None, or W >= 0 (causal only): row i sees keys i - W .. i.
 
     workspace: optional uint8 GPU tensor of >= prefill_workspace_bytes() bytes; with it the keys
     are rotated once into it (bf16 input with RoPE), without it the rotation is fused per tile."""
@@ -203,8 +214,8 @@ def prefill(q, k, v, table=None, *, causal=True, pos0=0, out=None, out_dtype=Non
         _need(workspace, "workspace")
         wsb = workspace.numel() * workspace.element_size()
     _check(_lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq,
-                             Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), tmax, _ptr(workspace), wsb,
-                             _stream(stream)),
+                             Hkv, S, D, 1 if causal else 0, pos0, _win(window), _ptr(table), tmax,
+                             _ptr(workspace), wsb, _stream(stream)),
            "attn_prefill")
     return out
 
@@ -226,8 +237,8 @@ def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
     return out
 
 
-def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, out=None, out_dtype=None, lse=None,
-                       stream=None):
+def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, window=None, out=None, out_dtype=None,
+                       lse=None, stream=None):
     """prefill() for keys already rotated by rotate_keys_f16 (same table and pos0)."""
     for t, n in ((q, "q"), (k_rot, "k_rot"), (v, "v"), (table, "table")):
         _need(t, n)
@@ -243,13 +254,13 @@ def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, out=None, out
     if lse is not None:
         _need(lse, "lse")
     _check(_lib.attn_prefill_prerotated(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(lse), _dt(out), B, Hq,
-                                        Hkv, S, D, 1 if causal else 0, pos0, _ptr(table), table.shape[0],
-                                        _stream(stream)), "attn_prefill_prerotated")
+                                        Hkv, S, D, 1 if causal else 0, pos0, _win(window), _ptr(table),
+                                        table.shape[0], _stream(stream)), "attn_prefill_prerotated")
     return out
 
 
-def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, out=None, out_dtype=None,
-                  lse=None, workspace=None, stream=None):
+def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, window=None, out=None,
+                  out_dtype=None, lse=None, workspace=None, stream=None):
     """Append a chunk (k_new, v_new [B, Hkv, Sq, D]) to the cache [B, Hkv, S_max, D] at rows
     pos0 .. pos0+Sq-1 (keys rotated there), then attend q [B, Hq, Sq, D] to cache rows
     [0, pos0 + Sq) with the causal mask aligned at the bottom right.  All bf16.
@@ -285,8 +296,8 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, out=No
         _need(workspace, "workspace")
         wsb = workspace.numel() * workspace.element_size()
     _check(_lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
-                                   _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _ptr(table), tmax,
-                                   _ptr(workspace), wsb, _stream(stream)), "attn_prefill_chunk")
+                                   _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _win(window), _ptr(table),
+                                   tmax, _ptr(workspace), wsb, _stream(stream)), "attn_prefill_chunk")
     return out
 
 
@@ -298,9 +309,11 @@ def decode_num_splits(B, Hq, Hkv, S_max, D, n_split=0) -> int:
     return int(_lib.attn_decode_num_splits(B, Hq, Hkv, S_max, D, n_split))
 
 
-def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, out=None, out_dtype=None,
-           lse=None, workspace=None, stream=None):
-    """One query per sequence (q [B, Hq, 1, D]) against the cache [B, Hkv, S_max, D]."""
+def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, window=None, out=None,
+           out_dtype=None, lse=None, workspace=None, stream=None):
+    """One query per sequence (q [B, Hq, 1, D]) against the cache [B, Hkv, S_max, D].
+
+    window: None, or W >= 0: only cache rows j >= q_pos[b] - W are seen."""
     for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len")):
         _need(t, n)
     B, Hq, one, D = q.shape
@@ -325,14 +338,14 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, out=
         _need(table, "table")
         tmax = table.shape[0]
     _check(_lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(q_pos),
-                            _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _ptr(table), tmax,
-                            n_split, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                            _stream(stream)), "attn_decode")
+                            _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _win(window),
+                            _ptr(table), tmax, n_split, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream)), "attn_decode")
     return out
 
 
-def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None, *, n_split=0, out=None,
-                 out_dtype=None, lse=None, workspace=None, stream=None):
+def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None, *, n_split=0, window=None,
+                 out=None, out_dtype=None, lse=None, workspace=None, stream=None):
     """decode() against a paged cache: pools [num_blocks, Hkv, block_size, D] and an int32 block
     table [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size])."""
     for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
@@ -366,7 +379,7 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None,
         tmax = table.shape[0]
     _check(_lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_blocks, bs, _ptr(block_table),
                                   max_blocks, _ptr(cache_len), _ptr(q_pos), _ptr(out), _ptr(lse), _dt(q), _dt(out),
-                                  B, Hq, Hkv, D, _ptr(table), tmax, n_split, _ptr(workspace),
+                                  B, Hq, Hkv, D, _win(window), _ptr(table), tmax, n_split, _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)),
            "attn_decode_paged")
     return out
