@@ -30,6 +30,11 @@ What it computes is the plain definition, written out with NumPy in float64:
   section 6.2: the cache lives in fixed-size physical blocks (16 tokens on the page) found
   through a per-sequence table, like virtual-memory pages.  Token t of sequence b is in block
   block_table[b][t // block_size], slot t % block_size; decode then proceeds as above.
+* RoPE frequency scaling -- "Transformer internals: attention without the mysticism"
+  (ninaddeshpande.com), "Rotary positional embeddings (RoPE)", and devthesis Problem 3,
+  "Superiority for Context Window Extension": to reach past the trained context, Position
+  Interpolation, NTK-aware scaling and YaRN change the rotation frequencies.  The pages give no
+  formulas; the published definitions are used (see RopeScaling).
 * Sliding window -- "Building Self-Attention and Transformer Engines" (codingpancake.com),
   section 6.4: each token attends only to the W tokens before it (W = 4096 on the page).  The
   reading taken: the query at position p sees the keys at positions p - W .. p (the W preceding
@@ -54,10 +59,13 @@ zero-Q prefix means, permutation equivariance, torch's CPU
 
 from __future__ import annotations
 
+import dataclasses
+import math
+
 import numpy as np
 
 __all__ = ["rope_frequencies", "rope", "attention", "decode", "round_bf16", "append_to_cache",
-           "attention_with_cache", "decode_paged"]
+           "attention_with_cache", "decode_paged", "RopeScaling", "rope_angles"]
 
 
 def rope_frequencies(D: int, base: float = 10000.0) -> np.ndarray:
@@ -68,22 +76,69 @@ def rope_frequencies(D: int, base: float = 10000.0) -> np.ndarray:
     return np.power(float(base), -2.0 * i / D)
 
 
-def rope(x: np.ndarray, positions, base: float = 10000.0) -> np.ndarray:
+@dataclasses.dataclass(frozen=True)
+class RopeScaling:
+    """A RoPE frequency scaling for contexts longer than the trained one (factor s >= 1).
+
+    kind "pi"   Position Interpolation (Chen et al. 2023): positions are divided by s, so the
+                angle of pair i at position m is (m / s) theta_i.
+    kind "ntk"  NTK-aware scaling: the base grows to base * s^(D / (D - 2)), which keeps the
+                highest frequency (i = 0) and divides the lowest (i = D/2 - 1) by exactly s.
+    kind "yarn" YaRN (Peng et al. 2023), "NTK-by-parts" with the attention temperature: with
+                wavelength lambda_i = 2 pi / theta_i and r_i = original_max_pos / lambda_i, the
+                ramp g_i = clip((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1) mixes
+                theta_i' = (1 - g_i) theta_i / s + g_i theta_i (long wavelengths interpolated,
+                short ones kept), and both q and k are scaled by 0.1 ln(s) + 1 (so the scores
+                by its square).
+    """
+    kind: str
+    factor: float
+    original_max_pos: int = 4096
+    beta_fast: float = 32.0
+    beta_slow: float = 1.0
+
+
+def rope_angles(D: int, positions, base: float = 10000.0, scaling=None):
+    """(angles [S, D/2], amplitude): pair i of the row at position m turns by angles[m, i] and is
+    scaled by amplitude (1 except for YaRN)."""
+    theta = rope_frequencies(D, base)
+    pos = np.asarray(positions, dtype=np.float64).reshape(-1)
+    amp = 1.0
+    if scaling is not None:
+        s = float(scaling.factor)
+        if s < 1.0:
+            raise ValueError("scaling factor must be >= 1")
+        if scaling.kind == "pi":
+            pos = pos / s
+        elif scaling.kind == "ntk":
+            theta = rope_frequencies(D, float(base) * s ** (D / (D - 2.0)))
+        elif scaling.kind == "yarn":
+            r = scaling.original_max_pos * theta / (2.0 * math.pi)
+            g = np.clip((r - scaling.beta_slow) / (scaling.beta_fast - scaling.beta_slow), 0.0, 1.0)
+            theta = (1.0 - g) * theta / s + g * theta
+            amp = 0.1 * math.log(s) + 1.0
+        else:
+            raise ValueError(f"unknown RoPE scaling {scaling.kind!r}")
+    return pos[:, None] * theta[None, :], amp
+
+
+def rope(x: np.ndarray, positions, base: float = 10000.0, scaling=None) -> np.ndarray:
     """Rotate adjacent pairs of the last axis of ``x`` (shape [..., S, D]) at ``positions`` [S].
 
     Pair i of the row at position m becomes
     (x_{2i} cos(m theta_i) - x_{2i+1} sin(m theta_i), x_{2i} sin(m theta_i) + x_{2i+1} cos(m theta_i)),
-    the counter-clockwise rotation R_{Theta,m}^{(i)} of devthesis section 3.
+    the counter-clockwise rotation R_{Theta,m}^{(i)} of devthesis section 3 (angles and an
+    amplitude from ``scaling`` when given, see RopeScaling).
     """
     x = np.asarray(x, dtype=np.float64)
     D = x.shape[-1]
-    theta = rope_frequencies(D, base)
-    pos = np.asarray(positions, dtype=np.float64).reshape(-1)
-    if pos.size != x.shape[-2]:
+    if D % 2:
+        raise ValueError("RoPE needs an even head dimension")
+    if np.asarray(positions).reshape(-1).size != x.shape[-2]:
         raise ValueError("one position per row")
-    ang = pos[:, None] * theta[None, :]          # [S, D/2], formed in float64
-    c = np.cos(ang)
-    s = np.sin(ang)
+    ang, amp = rope_angles(D, positions, base, scaling)   # [S, D/2], formed in float64
+    c = amp * np.cos(ang)
+    s = amp * np.sin(ang)
     x0 = x[..., 0::2]
     x1 = x[..., 1::2]
     out = np.empty_like(x)
@@ -114,7 +169,8 @@ def _softmax_rows(scores: np.ndarray):
     return w, lse[..., 0]
 
 
-def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0, rows=None, window=None):
+def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0, rows=None, window=None,
+              rope_scaling=None):
     """Prefill attention over [B, H, S, D] tensors, materialising every score row.
 
     q: [B, Hq, S, D]; k, v: [B, Hkv, S, D] (float64 or anything castable).
@@ -145,13 +201,13 @@ def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0,
     for b in range(B):
         k_rot = [None] * Hkv
         for kv in range(Hkv):
-            k_rot[kv] = rope(k[b, kv], pos0 + keys, rope_base) if rope_base is not None else k[b, kv]
+            k_rot[kv] = rope(k[b, kv], pos0 + keys, rope_base, rope_scaling) if rope_base is not None else k[b, kv]
         for h in range(Hq):
             kv = h // G
             r = rows[h]
             qh = q[b, h, r]
             if rope_base is not None:
-                qh = rope(qh, pos0 + r, rope_base)
+                qh = rope(qh, pos0 + r, rope_base, rope_scaling)
             s = (qh @ k_rot[kv].T) * scale                  # [n, S] full rows
             if causal:
                 s = np.where(keys[None, :] > r[:, None], -np.inf, s)
@@ -163,7 +219,7 @@ def attention(q, k, v, *, causal: bool = True, rope_base=10000.0, pos0: int = 0,
     return o, lse
 
 
-def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0, window=None):
+def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0, window=None, rope_scaling=None):
     """One query per sequence against a KV cache (keys already rotated; used as stored).
 
     q: [B, Hq, 1, D]; k_cache, v_cache: [B, Hkv, S_max, D]; cache_len, q_pos: [B] ints.
@@ -190,7 +246,7 @@ def decode(q, k_cache, v_cache, cache_len, q_pos, *, rope_base=10000.0, window=N
             continue
         qb = q[b, :, 0, :]                                   # [Hq, D]
         if rope_base is not None:
-            qb = rope(qb[:, None, :], [int(q_pos[b])], rope_base)[:, 0, :]
+            qb = rope(qb[:, None, :], [int(q_pos[b])], rope_base, rope_scaling)[:, 0, :]
         for kv in range(Hkv):
             qg = qb[kv * G:(kv + 1) * G]                     # [G, D]
             s = (qg @ kc[b, kv, :L].T) * scale               # [G, L]
@@ -217,7 +273,7 @@ def round_bf16(x) -> np.ndarray:
     return out
 
 
-def append_to_cache(k_cache, v_cache, k_new, v_new, pos0: int, *, rope_base=10000.0):
+def append_to_cache(k_cache, v_cache, k_new, v_new, pos0: int, *, rope_base=10000.0, rope_scaling=None):
     """Cache after a chunk of Sq new tokens is written into rows [pos0, pos0 + Sq).
 
     k_cache, v_cache: [B, Hkv, S_max, D]; k_new, v_new: [B, Hkv, Sq, D].  Key row s is rotated
@@ -231,13 +287,14 @@ def append_to_cache(k_cache, v_cache, k_new, v_new, pos0: int, *, rope_base=1000
     Sq = k_new.shape[2]
     if pos0 < 0 or pos0 + Sq > kc.shape[2]:
         raise ValueError("chunk does not fit the cache")
-    kr = rope(k_new, pos0 + np.arange(Sq), rope_base) if rope_base is not None else k_new
+    kr = rope(k_new, pos0 + np.arange(Sq), rope_base, rope_scaling) if rope_base is not None else k_new
     kc[:, :, pos0:pos0 + Sq] = round_bf16(kr)
     vc[:, :, pos0:pos0 + Sq] = v_new
     return kc, vc
 
 
-def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, rows=None, window=None):
+def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, rows=None, window=None,
+                         rope_scaling=None):
     """A chunk of Sq queries at positions pos0 .. pos0+Sq-1 against the cache rows [0, pos0 + Sq).
 
     q: [B, Hq, Sq, D] (rotated here at pos0 + i unless rope_base is None); k_cache, v_cache:
@@ -272,7 +329,7 @@ def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, r
             r = rows[h]
             qh = q[b, h, r]
             if rope_base is not None:
-                qh = rope(qh, pos0 + r, rope_base)
+                qh = rope(qh, pos0 + r, rope_base, rope_scaling)
             s = (qh @ kc[b, kv, :Sk].T) * scale                  # [n, pos0 + Sq] full rows
             s = np.where(keys[None, :] > pos0 + r[:, None], -np.inf, s)
             if window is not None:
@@ -283,7 +340,8 @@ def attention_with_cache(q, k_cache, v_cache, pos0: int, *, rope_base=10000.0, r
     return o, lse
 
 
-def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_base=10000.0, window=None):
+def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_base=10000.0, window=None,
+                 rope_scaling=None):
     """Decode against a paged KV cache.
 
     k_pages, v_pages: [num_blocks, Hkv, block_size, D] physical blocks; block_table: int
@@ -305,4 +363,4 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_bas
             blk = int(bt[b, t // bs])
             kc[b, :, t] = kp[blk, :, t % bs]
             vc[b, :, t] = vp[blk, :, t % bs]
-    return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base, window=window)
+    return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base, window=window, rope_scaling=rope_scaling)
