@@ -18,6 +18,8 @@ One step = one pass of the hot path over the workload's synthetic batch:
     16-token blocks scattered over a pool in a seeded random order; one attn_decode_paged call.
   * sliding window (sub-objects ``swa_prefill``, ``swa_decode``): the long-context prefill and
     the decode workload with a 4096-token window (a query sees the 4096 keys before it).
+  * multi-query decode (sub-object ``mqa_decode``): batch 32 over an 8192-token cache with one
+    KV head for 64 query heads.
   * chunk (sub-object ``chunk_prefill``): the last 2048-token chunk of an 8192-token GQA prompt
     (B=1, Hq=64, Hkv=8, D=128) against the 6144 tokens already in the KV cache; one
     attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
@@ -97,7 +99,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "swa", "all"], default="all")
+    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "swa", "mqa", "all"],
+                    default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -330,6 +333,8 @@ def main():
         res["swa"] = bench_prefill(lib, inputs, W["swa"], max(5, args.steps // 2), max(3, args.warmup // 2),
                                    variants=False)
         res["swa_decode"] = bench_decode(lib, inputs, W["swa_decode"], 4 * args.steps, 4 * args.warmup)
+    if args.only in ("mqa", "all"):
+        res["mqa_decode"] = bench_decode(lib, inputs, W["mqa_decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("paged", "all"):
         res["paged"] = bench_paged_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("chunk", "all"):
@@ -422,6 +427,14 @@ def main():
             "config": {"workload": "batch decode with a sliding window", "B": wl.B, "cache_len": wl.S, "Hq": wl.Hq,
                        "Hkv": wl.Hkv, "head_dim": wl.D, "window": wl.window,
                        "kv_bytes_per_step": wl.decode_kv_bytes()}}
+    if "mqa_decode" in res:
+        r = res["mqa_decode"]
+        wl = r["d"].wl
+        out["mqa_decode"] = {
+            "value": round(r["gbs"], 1), "unit": "GB/s", "ms_per_step": round(r["ms"], 5),
+            "frac": round(r["gbs"] / HBM_PEAK_GBS, 4), "n_split": r["n_split"],
+            "config": {"workload": "multi-query batch decode (one KV head)", "B": wl.B, "cache_len": wl.S,
+                       "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.D, "kv_bytes_per_step": wl.decode_kv_bytes()}}
     if "paged" in res:
         r = res["paged"]
         wl = r["wl"]

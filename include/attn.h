@@ -81,6 +81,30 @@ size_t attn_rope_table_bytes(int max_pos, int D);
 attn_status attn_rope_table_init(float* table, int max_pos, int D, double base, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * attn_rope_table_init_scaled: the same table with a frequency scaling for contexts longer
+ * than the trained one.  The pages name Position Interpolation, NTK-aware scaling and YaRN
+ * ("Transformer internals: attention without the mysticism", ninaddeshpande.com, "Rotary
+ * positional embeddings (RoPE)"; devthesis.com Problem 3, "Superiority for Context Window
+ * Extension") without formulas; these follow the methods' publications, with s = factor:
+ *   ATTN_ROPE_PLAIN  the plain table (factor and the rest ignored);
+ *   ATTN_ROPE_PI     angle (m / s) * theta_i;
+ *   ATTN_ROPE_NTK    theta_i from the base base * s^(D / (D - 2)) (D >= 4);
+ *   ATTN_ROPE_YARN   with r_i = original_max_pos * theta_i / (2 pi) and
+ *                    g_i = clamp((r_i - beta_slow) / (beta_fast - beta_slow), 0, 1):
+ *                    theta_i' = (1 - g_i) theta_i / s + g_i theta_i, and entries scaled by
+ *                    0.1 ln(s) + 1 (so scores by its square); usual betas 32 and 1.
+ * Every kernel reads its rotation from the table, so a scaled table works everywhere a table
+ * is taken; keys stored in a KV cache must have been rotated with the same table.
+ * Errors: as attn_rope_table_init, plus ATTN_ERR_INVALID_ARG for an unknown scaling,
+ * factor < 1 or not finite, NTK with D < 4, YaRN with original_max_pos < 1 or
+ * beta_fast <= beta_slow.
+ * --------------------------------------------------------------------------------------- */
+typedef enum { ATTN_ROPE_PLAIN = 0, ATTN_ROPE_PI = 1, ATTN_ROPE_NTK = 2, ATTN_ROPE_YARN = 3 } attn_rope_scaling;
+attn_status attn_rope_table_init_scaled(float* table, int max_pos, int D, double base,
+                                        attn_rope_scaling scaling, double factor, int original_max_pos,
+                                        double beta_fast, double beta_slow, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * attn_rope_apply: out[b,h,s,:] = RoPE(x[b,h,s,:]) at position pos0 + s
  * (devthesis section 3; the dim-8 example of "Transformer Architecture: FlashAttention &
  * RoPE", academy.kwas.tech).
@@ -203,7 +227,9 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
  * workspace: device scratch of at least attn_decode_workspace_bytes(...) bytes with the
  * same B, Hq, Hkv, S_max, D and n_split; its contents on entry do not matter.
  *
- * Support matrix: in_dt = ATTN_BF16, D in {64, 128}, out_dt either.
+ * Support matrix: in_dt = ATTN_BF16, D in {64, 128}, out_dt either; any group size Hq / Hkv
+ * (query heads are taken 16 at a time per workgroup; with more than 16 per KV head, as in
+ * multi-query attention, the groups of one KV head read its K/V back to back).
  * Errors: ATTN_ERR_INVALID_ARG for null pointers (q_pos may be NULL only without RoPE and
  * without a window), sizes < 1, Hq % Hkv != 0, n_split < 0, workspace too small, misalignment;
  * ATTN_ERR_UNSUPPORTED outside the support matrix.

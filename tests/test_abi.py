@@ -91,7 +91,7 @@ def _decode(**kw):
     (dict(B=0), INV), (dict(Hq=15), INV), (dict(S=0), INV), (dict(ns=-1), INV),
     (dict(wsb=16), INV), (dict(kc=MIS), INV), (dict(ws=MIS), INV), (dict(cl=P(0x10002)), INV),
     (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
-    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=3), INV),
     (dict(table=None, qp=None, window=100), INV),           # a window needs the query positions
 ])
 def test_decode_rejects(kw, code):
@@ -133,6 +133,17 @@ def test_two_stage_prefill_rejects():
     assert pre(D=64 + 32) == UNSUP
 
 
+def test_rope_table_init_scaled_rejects():
+    raw = lib.raw()
+    f = lambda table=A, mp=10, D=8, base=10000.0, kind=1, s=2.0, L=4096, bf=32.0, bs=1.0: \
+        raw.attn_rope_table_init_scaled(table, mp, D, base, kind, s, L, bf, bs, None)
+    assert f(kind=4) == INV and f(kind=-1) == INV
+    assert f(s=0.5) == INV and f(s=float("inf")) == INV and f(s=float("nan")) == INV
+    assert f(kind=2, D=2) == INV
+    assert f(kind=3, L=0) == INV and f(kind=3, bf=1.0, bs=1.0) == INV and f(kind=3, bf=float("nan")) == INV
+    assert f(table=None) == INV and f(table=MIS) == INV and f(D=7) == INV and f(base=1.0) == INV
+
+
 def test_rope_table_init_rejects():
     raw = lib.raw()
     assert raw.attn_rope_table_init(None, 10, 8, 10000.0, None) == INV
@@ -160,6 +171,10 @@ def test_decode_workspace_geometry():
     assert lib.decode_num_splits(1, 8, 1, 40, 64, 8) == 2
     assert lib.decode_num_splits(1, 8, 1, 1, 64, 0) == 1
     assert lib.decode_workspace_bytes(0, 8, 1, 100, 64, 0) == 0
+    # more than 16 query heads per KV head: groups of 16 count as units
+    assert lib.decode_num_splits(32, 64, 1, 8192, 128, 0) == 4    # 32 x 4 units x 4 splits = 512
+    assert lib.decode_num_splits(64, 64, 1, 8192, 128, 0) == 1    # 256 units
+    assert lib.decode_num_splits(4, 64, 3, 100, 128, 0) == 0      # Hq not a multiple of Hkv
 
 
 def _chunk(**kw):
@@ -209,7 +224,7 @@ def _paged(**kw):
     (dict(bs=8), INV), (dict(bs=24), INV), (dict(bs=0), INV), (dict(bs=8192), INV),
     (dict(wsb=16), INV), (dict(kp=MIS), INV), (dict(ws=MIS), INV), (dict(bt=P(0x10002)), INV),
     (dict(cl=P(0x10002)), INV), (dict(table=MIS), INV), (dict(tmax=0), INV), (dict(D=63), INV),
-    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=2), UNSUP),
+    (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP), (dict(Hq=64, Hkv=3), INV),
     (dict(table=None, qp=None, window=0), INV),
 ])
 def test_decode_paged_rejects(kw, code):

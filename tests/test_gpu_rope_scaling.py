@@ -1,0 +1,157 @@
+"""RoPE frequency scalings (position interpolation, NTK-aware, YaRN) and multi-query attention
+(one KV head for every query head) on the GPU, against the fp64 oracle.
+
+The scalings only change the coefficient table, so they are checked at the table itself and
+then through every kernel that reads a table (prefill, chunk with its key append, decode).
+Multi-query decode takes the query heads 16 at a time, so group sizes of 20, 32 and 64 are
+covered, split and unsplit, contiguous and paged.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from conftest import assert_bf16_parity, banner, err_stats, to_np
+from transformer_self_attention_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+SCALINGS = {
+    "pi": (dict(scaling="pi", factor=4.0), oracle.RopeScaling("pi", 4.0)),
+    "ntk": (dict(scaling="ntk", factor=8.0), oracle.RopeScaling("ntk", 8.0)),
+    "yarn": (dict(scaling="yarn", factor=4.0, original_max_pos=2048),
+             oracle.RopeScaling("yarn", 4.0, original_max_pos=2048)),
+}
+
+
+@pytest.fixture(scope="module")
+def lib():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from transformer_self_attention_amd import lib as L
+    return L
+
+
+@pytest.mark.parametrize("name", sorted(SCALINGS))
+@pytest.mark.parametrize("D", [64, 128])
+def test_scaled_table_against_fp64(lib, name, D):
+    banner(f"rope table {name} D={D}")
+    kw, sc = SCALINGS[name]
+    tab = lib.make_rope_table(8192, D, **kw)
+    torch.cuda.synchronize()
+    got = tab.cpu().numpy().astype(np.float64)
+    ang, amp = oracle.rope_angles(D, np.arange(8192), scaling=sc)
+    # one float32 rounding of values of magnitude <= amp
+    assert np.abs(got[..., 0] - amp * np.cos(ang)).max() <= amp * 2.0 ** -24 * 1.01
+    assert np.abs(got[..., 1] - amp * np.sin(ang)).max() <= amp * 2.0 ** -24 * 1.01
+
+
+@pytest.mark.parametrize("name", sorted(SCALINGS))
+@pytest.mark.parametrize("mode", ["workspace", "fused"])
+def test_prefill_with_scaled_table(lib, name, mode):
+    banner(f"prefill with {name} table, mode={mode}")
+    kw, sc = SCALINGS[name]
+    wl = inputs.Workload("r", B=2, Hq=8, Hkv=2, S=333, D=128, dtype="bf16", seed=51, kind="prefill")
+    p = inputs.make_prefill(wl)
+    tab = lib.make_rope_table(1000 + wl.S, wl.D, **kw)
+    ws = None
+    if mode == "workspace":
+        ws = torch.empty(lib.prefill_workspace_bytes(2, 2, wl.S, 128), dtype=torch.uint8, device="cuda")
+    o = lib.prefill(p.q.torch("cuda"), p.k.torch("cuda"), p.v.torch("cuda"), tab, pos0=1000,
+                    out_dtype=torch.float32, workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attention(p.q.f64(), p.k.f64(), p.v.f64(), pos0=1000, rope_scaling=sc)
+    assert_bf16_parity(to_np(o), ref, f"o ({name})")
+
+
+def test_chunk_and_decode_with_yarn_table(lib):
+    """A chunk appended with a YaRN table, then a decode step with the same table."""
+    kw, sc = SCALINGS["yarn"]
+    banner("chunk + decode with a YaRN table")
+    wl = inputs.Workload("c", B=2, Hq=8, Hkv=2, S=150, D=128, dtype="bf16", seed=52, kind="chunk",
+                         pos0=5000, S_max=5200)
+    c = inputs.make_chunk(wl)
+    tab = lib.make_rope_table(wl.S_max + 1, 128, **kw)
+    kc, vc = c.k_cache.torch("cuda"), c.v_cache.torch("cuda")
+    o = lib.prefill_chunk(c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda"), kc, vc, wl.pos0, tab,
+                          out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_k, ref_v = oracle.append_to_cache(c.k_cache.f64(), c.v_cache.f64(), c.k_new.f64(), c.v_new.f64(), wl.pos0,
+                                          rope_scaling=sc)
+    ref, _ = oracle.attention_with_cache(c.q.f64(), ref_k, ref_v, wl.pos0, rope_scaling=sc)
+    assert_bf16_parity(to_np(o), ref, "chunk o (yarn)")
+    L = wl.pos0 + wl.S
+    d = inputs.make_decode(inputs.Workload("d", B=2, Hq=8, Hkv=2, S=1, D=128, dtype="bf16", seed=53, kind="decode"))
+    cl = torch.full((2,), L, dtype=torch.int32, device="cuda")
+    od = lib.decode(d.q.torch("cuda"), kc, vc, cl, cl.clone(), tab, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref_d, _ = oracle.decode(d.q.f64(), ref_k, ref_v, [L] * 2, [L] * 2, rope_scaling=sc)
+    assert_bf16_parity(to_np(od), ref_d, "decode o (yarn)")
+
+
+# ------------------------------------------------------------------------------------------
+# Multi-query attention: one KV head
+# ------------------------------------------------------------------------------------------
+def test_mqa_prefill(lib):
+    banner("prefill MQA B=1 Hq=32 Hkv=1 S=4096 (256 rows/head)")
+    wl = inputs.Workload("m", B=1, Hq=32, Hkv=1, S=4096, D=128, dtype="bf16", seed=54, kind="prefill",
+                         check_rows=256)
+    p = inputs.make_prefill(wl)
+    tab = lib.make_rope_table(wl.S, 128)
+    ws = torch.empty(lib.prefill_workspace_bytes(1, 1, wl.S, 128), dtype=torch.uint8, device="cuda")
+    o = lib.prefill(p.q.torch("cuda"), p.k.torch("cuda"), p.v.torch("cuda"), tab, out_dtype=torch.float32,
+                    workspace=ws)
+    torch.cuda.synchronize()
+    ref, _ = oracle.attention(p.q.f64(), p.k.f64(), p.v.f64(), rows=p.rows)
+    got = to_np(o)
+    assert_bf16_parity(np.stack([got[:, h, p.rows[h]] for h in range(32)], axis=1), ref, "mqa prefill o")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,lens,n_split", [
+    (3, 64, 1, 1000, [1000, 517, 1], 0),      # 4 groups of 16 query heads per KV head
+    (2, 20, 1, 700, [700, 333], 3),           # a group of 16 and one of 4
+    (2, 64, 2, 600, [600, 599], 1),           # 32 per KV head, one split
+    (4, 32, 1, 2000, [2000, 1999, 1000, 0], 0),
+])
+def test_decode_large_groups(lib, B, Hq, Hkv, S, lens, n_split):
+    banner(f"decode G={Hq // Hkv} B={B} Hq={Hq} Hkv={Hkv} S={S} n_split={n_split}")
+    wl = inputs.Workload("d", B=B, Hq=Hq, Hkv=Hkv, S=S, D=128, dtype="bf16", seed=S + Hq, kind="decode")
+    lens = np.array(lens, np.int32)
+    d = inputs.make_decode(wl, cache_len=lens, q_pos=lens + 3)
+    tab = lib.make_rope_table(int(lens.max()) + 4, 128)
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    o = lib.decode(d.q.torch("cuda"), d.k_cache.torch("cuda"), d.v_cache.torch("cuda"),
+                   torch.from_numpy(lens).cuda(), torch.from_numpy(lens + 3).cuda(), tab, n_split=n_split,
+                   out_dtype=torch.float32, lse=lse)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode(d.q.f64(), d.k_cache.f32, d.v_cache.f32, lens, lens + 3)
+    assert_bf16_parity(to_np(o), ref, "o")
+    got_lse = to_np(lse)
+    empty = lens <= 0
+    assert np.all(np.isneginf(got_lse[empty]))
+    assert err_stats(got_lse[~empty], ref_lse[~empty])[0] < 2e-2
+    # paged: the same cache in blocks, bit-identical
+    pd = inputs.make_paged_decode(wl, block_size=16, cache_len=lens, q_pos=lens + 3)
+    op = lib.decode_paged(pd.q.torch("cuda"), pd.k_pages.torch("cuda"), pd.v_pages.torch("cuda"),
+                          torch.from_numpy(pd.block_table).cuda(), torch.from_numpy(lens).cuda(),
+                          torch.from_numpy(lens + 3).cuda(), tab, n_split=n_split, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    if S % 16 == 0:
+        assert torch.equal(op, o)
+    else:
+        assert_bf16_parity(to_np(op), ref, "paged o")
+
+
+def test_mqa_decode_config(lib):
+    """Batch-32 decode over an 8192-token cache with one KV head for 64 query heads."""
+    wl = inputs.WORKLOADS["mqa_decode"]
+    banner("decode MQA B=32 Hq=64 Hkv=1 cache=8192 (full config)")
+    d = inputs.make_decode(wl)
+    tab = lib.make_rope_table(int(d.q_pos.max()) + 1, 128)
+    o = lib.decode(d.q.torch("cuda"), d.k_cache.torch("cuda"), d.v_cache.torch("cuda"),
+                   torch.from_numpy(d.cache_len).cuda(), torch.from_numpy(d.q_pos).cuda(), tab)
+    torch.cuda.synchronize()
+    ref, _ = oracle.decode(d.q.f64(), d.k_cache.f32, d.v_cache.f32, d.cache_len, d.q_pos)
+    assert_bf16_parity(to_np(o), ref, "mqa decode o")

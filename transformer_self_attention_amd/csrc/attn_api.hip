@@ -30,15 +30,16 @@ attn_status check_rope(const float* table, int table_max_pos, int pos0, int S) {
   return ATTN_OK;
 }
 
-// Decode split geometry: keys per split are a multiple of the 32-key wave block.
-void decode_geometry(int B, int Hkv, int S_max, int n_split_req, int* n_split, int* chunk) {
+// Decode split geometry: keys per split are a multiple of the 32-key wave block.  A unit is a
+// (sequence, KV head, group of up to 16 query heads) triple: one workgroup per unit and split.
+void decode_geometry(int B, int Hq, int Hkv, int S_max, int n_split_req, int* n_split, int* chunk) {
   int ns = n_split_req;
   if (ns <= 0) {
-    // With >= 256 (sequence, KV head) units, one 8-wave workgroup per unit streams the whole
+    // With >= 256 units, one 8-wave workgroup per unit streams the whole
     // cache and writes o directly (no merge pass).  Below that, split the cache over 4-wave
     // workgroups, aiming for >= 512 of them (2 per CU) with >= 256 keys per split.  Measured on
     // batch 32 x 8 KV heads x 8192 keys: one split, 158 us; 2 splits + merge, 165 us; 4, 168 us.
-    const int64_t units = (int64_t)B * Hkv;
+    const int64_t units = (int64_t)B * Hkv * ((Hq / Hkv + 15) / 16);
     int64_t want = units >= 256 ? 1 : (512 + units - 1) / units;
     int64_t cap = S_max / 256;
     if (cap < 1) cap = 1;
@@ -78,9 +79,34 @@ size_t attn_rope_table_bytes(int max_pos, int D) {
 }
 
 attn_status attn_rope_table_init(float* table, int max_pos, int D, double base, void* stream) {
+  return attn_rope_table_init_scaled(table, max_pos, D, base, ATTN_ROPE_PLAIN, 1.0, 1, 32.0, 1.0, stream);
+}
+
+attn_status attn_rope_table_init_scaled(float* table, int max_pos, int D, double base, attn_rope_scaling scaling,
+                                        double factor, int original_max_pos, double beta_fast,
+                                        double beta_slow, void* stream) {
   if (!table || !aligned16(table) || max_pos < 1 || D < 2 || (D & 1)) return ATTN_ERR_INVALID_ARG;
   if (!(base > 1.0) || !std::isfinite(base)) return ATTN_ERR_INVALID_ARG;
-  return from_hip(attn::launch_rope_table(table, max_pos, D, base, (hipStream_t)stream));
+  attn::RopeScalingArgs sc;
+  sc.kind = attn::kRopePlain;
+  sc.factor = 1.0;
+  sc.original_max_pos = 1.0;
+  sc.beta_fast = 32.0;
+  sc.beta_slow = 1.0;
+  if (scaling != ATTN_ROPE_PLAIN) {
+    if (scaling != ATTN_ROPE_PI && scaling != ATTN_ROPE_NTK && scaling != ATTN_ROPE_YARN) return ATTN_ERR_INVALID_ARG;
+    if (!(factor >= 1.0) || !std::isfinite(factor)) return ATTN_ERR_INVALID_ARG;
+    if (scaling == ATTN_ROPE_NTK && D < 4) return ATTN_ERR_INVALID_ARG;
+    if (scaling == ATTN_ROPE_YARN &&
+        (original_max_pos < 1 || !std::isfinite(beta_fast) || !std::isfinite(beta_slow) || !(beta_fast > beta_slow)))
+      return ATTN_ERR_INVALID_ARG;
+    sc.kind = scaling == ATTN_ROPE_PI ? attn::kRopePI : (scaling == ATTN_ROPE_NTK ? attn::kRopeNTK : attn::kRopeYaRN);
+    sc.factor = factor;
+    sc.original_max_pos = (double)original_max_pos;
+    sc.beta_fast = beta_fast;
+    sc.beta_slow = beta_slow;
+  }
+  return from_hip(attn::launch_rope_table(table, max_pos, D, base, sc, (hipStream_t)stream));
 }
 
 attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int H, int S, int D,
@@ -215,17 +241,17 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {
-  (void)Hq; (void)D;
-  if (B < 1 || Hkv < 1 || S_max < 1 || n_split < 0) return 0;
+  (void)D;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 || n_split < 0) return 0;
   int ns, chunk;
-  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
   return ns;
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int Hkv, int S_max, int D, int n_split) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return 0;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 || D < 1 || n_split < 0) return 0;
   int ns, chunk;
-  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
   const size_t parts = (size_t)B * Hq * ns;
   return parts * (size_t)D * sizeof(float) + parts * 2 * sizeof(float);
 }
@@ -250,11 +276,10 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
     return ATTN_ERR_INVALID_ARG;
   if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)B * Hkv * S_max * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
 
   int ns, chunk;
-  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
   attn::DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache;
   a.cache_len = cache_len; a.q_pos = q_pos;
@@ -296,11 +321,10 @@ attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_
   if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split)) return ATTN_ERR_INVALID_ARG;
   if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
   if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-  if (Hq / Hkv > 16) return ATTN_ERR_UNSUPPORTED;
   if ((int64_t)num_blocks * Hkv * block_size * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
 
   int ns, chunk;
-  decode_geometry(B, Hkv, S_max, n_split, &ns, &chunk);
+  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
   attn::DecodeArgs a;
   a.q = q; a.k = k_pages; a.v = v_pages;
   a.cache_len = cache_len; a.q_pos = q_pos;

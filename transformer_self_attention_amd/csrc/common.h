@@ -56,7 +56,17 @@ __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_rea
 // Launchers (each returns hipGetLastError() of its launch).  Arguments were validated by the
 // C-ABI layer; the launchers only size grids.
 // ------------------------------------------------------------------------------------------
-hipError_t launch_rope_table(float* table, int max_pos, int D, double base, hipStream_t st);
+// RoPE frequency scaling of the coefficient table (kind: kRopePlain, kRopePI, kRopeNTK, kRopeYaRN).
+enum { kRopePlain = 0, kRopePI = 1, kRopeNTK = 2, kRopeYaRN = 3 };
+struct RopeScalingArgs {
+  int kind;
+  double factor;            // s >= 1
+  double original_max_pos;  // YaRN: the trained context length
+  double beta_fast, beta_slow;
+};
+
+hipError_t launch_rope_table(float* table, int max_pos, int D, double base, const RopeScalingArgs& sc,
+                             hipStream_t st);
 
 hipError_t launch_rope_apply(const void* x, void* out, bool bf16, int64_t rows, int S, int D,
                              int pos0, const float* table, hipStream_t st);

@@ -7,7 +7,11 @@
 // (devthesis.com section 3) at its own position.  The G = Hq/Hkv query heads that share a KV head
 // (codingpancake.com section 6.1) are processed together so each K/V byte is read once.
 //
-// decode_split_kernel, one workgroup per (sequence, KV head, split):
+// decode_split_kernel, one workgroup per (sequence, KV head, group of up to 16 query heads, split):
+//  * The G query heads of a KV head fill the 16 columns of the MFMA B operand; with G > 16 (as in
+//    multi-query attention, one KV head for every query head) they are taken 16 at a time by
+//    separate workgroups.  Those workgroups get consecutive slots on the same XCD (workgroup ids
+//    are dealt to the 8 XCDs in turn), so their reads of the same K/V meet in that XCD's L2.
 //  * The waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
 //    flight while sub-block i is consumed (16 x 16-byte loads per lane).  The cache is read once,
 //    so its loads are nontemporal (streaming) and do not displace reusable lines in the caches.
@@ -45,6 +49,7 @@ namespace {
 constexpr int kWavesSplit = 4;   // waves per workgroup when the cache is split (merge pass after)
 constexpr int kWavesWhole = 8;   // waves per workgroup when one workgroup covers the whole cache
 constexpr int kSub = 32;   // keys per wave iteration
+constexpr int kNumXcd = 8;  // workgroup ids are dealt to the XCDs in turn
 constexpr float kRescaleThreshold = 8.0f;
 
 // max / sum partners across the 16-lane rows of a wave.
@@ -72,10 +77,12 @@ __device__ __forceinline__ int vswz(int r, int lc) {  // 16 chunks per row (D = 
 // NW waves per workgroup.  WHOLE: one split covers the whole cache, and the workgroup writes the
 // final o (OUT_BF16 selects its type) and lse itself; otherwise it writes one partial (m, l, O)
 // per (row, split) for decode_merge_kernel.
-template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16, bool PAGED>
+// STREAM: K/V are read once (nontemporal loads); off when several workgroups share a KV head
+// (more than 16 query heads per KV head), whose repeated reads should stay in L2.
+template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16, bool PAGED, bool STREAM>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
-    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int Hq, int Hkv,
+    const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int B, int Hq, int Hkv,
     int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse,
     const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks, int window) {
@@ -92,8 +99,20 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kWaves][kSub * D];
   __shared__ float red_ml[kWaves][16][2];
 
-  const int split = blockIdx.x, hkv = blockIdx.y, b = blockIdx.z;
+  // workgroup id -> (unit, sub-group): the n_sub workgroups of a unit share id % 8 (one XCD)
   const int G = Hq / Hkv;
+  const int n_sub = (G + 15) / 16;               // groups of 16 query heads per KV head
+  const int n_units = n_split * Hkv * B;
+  const int wid = blockIdx.x;
+  const int jx = wid / kNumXcd;
+  const int sub = jx % n_sub;
+  const int unit = (jx / n_sub) * kNumXcd + wid % kNumXcd;
+  if (unit >= n_units) return;
+  const int split = unit % n_split;
+  const int hkv = (unit / n_split) % Hkv;
+  const int b = unit / (n_split * Hkv);
+  const int h0 = hkv * G + sub * 16;             // first query head of this workgroup
+  const int Gs = min(16, G - sub * 16);          // query heads of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, i16 = lane & 15;
   const int qrow = i16;  // this lane's query row in the group (B-operand column / C column)
@@ -117,8 +136,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       pos = q_pos[b];
       if (pos < 0 || pos >= table_max_pos) pos = 0;  // such rows are written as NaN at the end
     }
-    const bool valid = qrow < G;
-    const uint16_t* qp = q + ((int64_t)b * Hq + hkv * G + (valid ? qrow : 0)) * D;
+    const bool valid = qrow < Gs;
+    const uint16_t* qp = q + ((int64_t)b * Hq + h0 + (valid ? qrow : 0)) * D;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 32 * ks + 8 * g16;
@@ -188,7 +207,10 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       else row = ok ? key : kbeg;
       const uint16_t* kp = kg + row * D + 8 * g16;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) kst[kb][ks] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(kp + 32 * ks));
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(kp + 32 * ks);
+        kst[kb][ks] = STREAM ? __builtin_nontemporal_load(src) : *src;
+      }
     }
 #pragma unroll
     for (int i = 0; i < LPT; ++i) {
@@ -198,7 +220,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       int64_t row;
       if constexpr (PAGED) row = ok ? ((c / NCH) >= 16 ? r1 : r0) + ((c / NCH) & 15) : r0;
       else row = ok ? key : kbeg;
-      vst[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vg + row * D + (c % NCH) * 8));
+      const u32x4* src = reinterpret_cast<const u32x4*>(vg + row * D + (c % NCH) * 8);
+      vst[i] = STREAM ? __builtin_nontemporal_load(src) : *src;
       if (!ok) vst[i] = u32x4{0, 0, 0, 0};
     }
   };
@@ -309,7 +332,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   __syncthreads();
 
   // thread -> (row, d) pairs of the merged partial
-  for (int e = tid; e < G * D; e += kThreads) {
+  for (int e = tid; e < Gs * D; e += kThreads) {
     const int rr = e / D, d = e % D;
     float M = -INFINITY;
 #pragma unroll
@@ -330,15 +353,15 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
         const int p = q_pos[b];
         if (p < 0 || p >= table_max_pos) { out = __builtin_nanf(""); ls = __builtin_nanf(""); }
       }
-      const int64_t oi = ((int64_t)b * Hq + hkv * G + rr) * D + d;
+      const int64_t oi = ((int64_t)b * Hq + h0 + rr) * D + d;
       if constexpr (OUT_BF16) {
         reinterpret_cast<__bf16*>(o)[oi] = (__bf16)out;
       } else {
         reinterpret_cast<float*>(o)[oi] = out;
       }
-      if (lse && d == 0) lse[(int64_t)b * Hq + hkv * G + rr] = ls;
+      if (lse && d == 0) lse[(int64_t)b * Hq + h0 + rr] = ls;
     } else {
-      const int64_t part = (((int64_t)b * Hq + hkv * G + rr) * n_split + split);
+      const int64_t part = (((int64_t)b * Hq + h0 + rr) * n_split + split);
       ws_o[part * D + d] = acc;
       if (d == 0) {
         ws_ml[part * 2 + 0] = M;
@@ -379,29 +402,32 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   if (lse && d == 0) lse[(int64_t)b * Hq + h] = ls;
 }
 
-template <int D, bool ROPE, bool PAGED>
+template <int D, bool ROPE, bool PAGED, bool STREAM>
 hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* kc = (const uint16_t*)a.k;
   const uint16_t* vc = (const uint16_t*)a.v;
   const float2* tab = reinterpret_cast<const float2*>(a.table);
+  const int n_sub = (a.Hq / a.Hkv + 15) / 16;
+  const int64_t n_units = (int64_t)a.n_split * a.Hkv * a.B;
+  const unsigned grid = (unsigned)(((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * n_sub);
   if (a.n_split == 1) {
     // one workgroup per (sequence, KV head) streams the whole cache and writes o itself
     if (a.out_bf16)
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED>), dim3(1, a.Hkv, a.B),
-                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED, STREAM>), dim3(grid),
+                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
                          a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     else
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED>), dim3(1, a.Hkv, a.B),
-                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.Hq, a.Hkv, a.S_max,
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED, STREAM>), dim3(grid),
+                         dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
                          a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED>),
-                     dim3(a.n_split, a.Hkv, a.B), dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
-                     a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse,
+  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED, STREAM>),
+                     dim3(grid), dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
+                     a.B, a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse,
                      a.block_table, a.max_blocks, a.bs_log2, a.num_blocks, a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -414,17 +440,19 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool PAGED>
+template <bool PAGED, bool STREAM>
 hipError_t go_d(const DecodeArgs& a, hipStream_t st) {
   const bool rope = a.table != nullptr;
-  if (a.D == 64) return rope ? go<64, true, PAGED>(a, st) : go<64, false, PAGED>(a, st);
-  return rope ? go<128, true, PAGED>(a, st) : go<128, false, PAGED>(a, st);
+  if (a.D == 64) return rope ? go<64, true, PAGED, STREAM>(a, st) : go<64, false, PAGED, STREAM>(a, st);
+  return rope ? go<128, true, PAGED, STREAM>(a, st) : go<128, false, PAGED, STREAM>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  return a.block_table ? go_d<true>(a, st) : go_d<false>(a, st);
+  const bool stream = a.Hq / a.Hkv <= 16;
+  if (a.block_table) return stream ? go_d<true, true>(a, st) : go_d<true, false>(a, st);
+  return stream ? go_d<false, true>(a, st) : go_d<false, false>(a, st);
 }
 
 }  // namespace attn

@@ -6,6 +6,13 @@
 // The frequencies match the NumPy example of "Transformer Architecture: FlashAttention & RoPE"
 // (academy.kwas.tech).
 //
+// Frequency scalings for contexts past the trained length (named on ninaddeshpande.com "Transformer
+// internals", "Rotary positional embeddings (RoPE)", and devthesis Problem 3; formulas from their
+// publications): position interpolation divides positions by the factor s; NTK-aware scaling
+// raises the base to base * s^(D/(D-2)); YaRN interpolates each pair by its wavelength (ramp over
+// r = original context / wavelength between beta_slow and beta_fast) and scales cos and sin by
+// 0.1 ln(s) + 1.  Only the table changes: every kernel reads the rotation from it.
+//
 // rope_apply is HBM-bound: it reads and writes every element once (plus the table row, which
 // stays in L2 across heads).  Each lane moves 16 bytes of x for bf16 (4 pairs) or fp32
 // (2 pairs), so loads and stores are dwordx4 and coalesced along D.
@@ -13,27 +20,44 @@
 
 namespace attn {
 
-// table[m][i] = (cos(m * theta_i), sin(m * theta_i)); angle formed in double precision.
-__global__ void rope_table_kernel(float2* __restrict__ table, int max_pos, int half, double base) {
+// table[m][i] = amp * (cos(a), sin(a)), a = m * theta_i (plain), with the scaling applied to m,
+// theta_i and amp as above; every step in double precision, rounded once to float.
+__global__ void rope_table_kernel(float2* __restrict__ table, int max_pos, int half, double base,
+                                  RopeScalingArgs sc) {
   const int64_t n = (int64_t)max_pos * half;
+  const double D = 2.0 * half;
+  const double kPi = 3.14159265358979323846;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int m = (int)(idx / half);
     const int i = (int)(idx - (int64_t)m * half);
-    const double theta = pow(base, -2.0 * (double)i / (double)(2 * half));
-    const double ang = (double)m * theta;
-    table[idx] = make_float2((float)cos(ang), (float)sin(ang));
+    double theta = pow(base, -2.0 * (double)i / D);
+    double pos = (double)m, amp = 1.0;
+    if (sc.kind == kRopePI) {
+      pos = (double)m / sc.factor;
+    } else if (sc.kind == kRopeNTK) {
+      theta = pow(base * pow(sc.factor, D / (D - 2.0)), -2.0 * (double)i / D);
+    } else if (sc.kind == kRopeYaRN) {
+      const double r = sc.original_max_pos * theta / (2.0 * kPi);
+      double g = (r - sc.beta_slow) / (sc.beta_fast - sc.beta_slow);
+      g = g < 0.0 ? 0.0 : (g > 1.0 ? 1.0 : g);
+      theta = (1.0 - g) * theta / sc.factor + g * theta;
+      amp = 0.1 * log(sc.factor) + 1.0;
+    }
+    const double ang = pos * theta;
+    table[idx] = make_float2((float)(amp * cos(ang)), (float)(amp * sin(ang)));
   }
 }
 
-hipError_t launch_rope_table(float* table, int max_pos, int D, double base, hipStream_t st) {
+hipError_t launch_rope_table(float* table, int max_pos, int D, double base, const RopeScalingArgs& sc,
+                             hipStream_t st) {
   const int half = D / 2;
   const int64_t n = (int64_t)max_pos * half;
   const int threads = 256;
   int64_t blocks = (n + threads - 1) / threads;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(threads), 0, st,
-                     reinterpret_cast<float2*>(table), max_pos, half, base);
+                     reinterpret_cast<float2*>(table), max_pos, half, base, sc);
   return hipGetLastError();
 }
 

@@ -90,6 +90,8 @@ WORKLOADS = {
                     check_rows=128, window=4096),
     "swa_decode": Workload("swa_decode", B=32, Hq=64, Hkv=8, S=8192, D=128, dtype="bf16", seed=3, kind="decode",
                            window=4096),
+    # multi-query decode: one KV head for all 64 query heads
+    "mqa_decode": Workload("mqa_decode", B=32, Hq=64, Hkv=1, S=8192, D=128, dtype="bf16", seed=7, kind="decode"),
     # the last 2048-token chunk of an 8192-token GQA prompt, against the 6144 tokens already cached
     "chunk": Workload("chunk", B=1, Hq=64, Hkv=8, S=2048, D=128, dtype="bf16", seed=5, kind="chunk",
                       check_rows=128, pos0=6144, S_max=8192),

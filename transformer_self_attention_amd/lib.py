@@ -24,6 +24,7 @@ EXPORTED = (
     "attn_status_string",
     "attn_rope_table_bytes",
     "attn_rope_table_init",
+    "attn_rope_table_init_scaled",
     "attn_rope_apply",
     "attn_prefill_workspace_bytes",
     "attn_prefill",
@@ -57,6 +58,9 @@ def _load():
     lib.attn_rope_table_bytes.argtypes = [i32, i32]
     lib.attn_rope_table_init.restype = i32
     lib.attn_rope_table_init.argtypes = [fp, i32, i32, ctypes.c_double, vp]
+    lib.attn_rope_table_init_scaled.restype = i32
+    lib.attn_rope_table_init_scaled.argtypes = [fp, i32, i32, ctypes.c_double, i32, ctypes.c_double, i32,
+                                                ctypes.c_double, ctypes.c_double, vp]
     lib.attn_rope_apply.restype = i32
     lib.attn_rope_apply.argtypes = [vp, vp, i32, i32, i32, i32, i32, i32, fp, i32, vp]
     lib.attn_prefill_workspace_bytes.restype = sz
@@ -148,18 +152,33 @@ def rope_table_bytes(max_pos: int, D: int) -> int:
     return int(_lib.attn_rope_table_bytes(max_pos, D))
 
 
-def rope_table_init(table: torch.Tensor, max_pos: int, D: int, base: float = 10000.0, stream=None):
-    """Fill float32 table [max_pos, D/2, 2] with (cos, sin) of m * base^(-2i/D)."""
+ROPE_SCALINGS = {"pi": 1, "ntk": 2, "yarn": 3}
+
+
+def rope_table_init(table: torch.Tensor, max_pos: int, D: int, base: float = 10000.0, stream=None, *,
+                    scaling: str = None, factor: float = 1.0, original_max_pos: int = 4096,
+                    beta_fast: float = 32.0, beta_slow: float = 1.0):
+    """Fill float32 table [max_pos, D/2, 2] with (cos, sin) of m * base^(-2i/D); scaling "pi",
+    "ntk" or "yarn" (with factor s and, for YaRN, the trained context and ramp ends) stretches
+    it for longer contexts (attn_rope_table_init_scaled)."""
     _need(table, "table")
     if table.dtype != torch.float32 or table.numel() * 4 < rope_table_bytes(max_pos, D):
         raise ValueError("table must be float32 with at least rope_table_bytes() bytes")
-    _check(_lib.attn_rope_table_init(_ptr(table), max_pos, D, float(base), _stream(stream)),
-           "attn_rope_table_init")
+    if scaling is None:
+        _check(_lib.attn_rope_table_init(_ptr(table), max_pos, D, float(base), _stream(stream)),
+               "attn_rope_table_init")
+        return
+    if scaling not in ROPE_SCALINGS:
+        raise ValueError(f"scaling must be one of {sorted(ROPE_SCALINGS)}")
+    _check(_lib.attn_rope_table_init_scaled(_ptr(table), max_pos, D, float(base), ROPE_SCALINGS[scaling],
+                                            float(factor), int(original_max_pos), float(beta_fast),
+                                            float(beta_slow), _stream(stream)), "attn_rope_table_init_scaled")
 
 
-def make_rope_table(max_pos: int, D: int, base: float = 10000.0, device="cuda", stream=None) -> torch.Tensor:
+def make_rope_table(max_pos: int, D: int, base: float = 10000.0, device="cuda", stream=None,
+                    **scaling) -> torch.Tensor:
     t = torch.empty((max_pos, D // 2, 2), dtype=torch.float32, device=device)
-    rope_table_init(t, max_pos, D, base, stream)
+    rope_table_init(t, max_pos, D, base, stream, **scaling)
     return t
 
 
