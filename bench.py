@@ -59,11 +59,11 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 158333.0 KiB, WRITE_SIZE 131086.6 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 458498662, "sources_sha256_16": "cb0f9f15ae093d17"},
+    # FETCH_SIZE 158235.2 KiB, WRITE_SIZE 131081.8 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 458293452, "sources_sha256_16": "49fb1668ac2746b5"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
-    # FETCH_SIZE 524914.4 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1075548979, "sources_sha256_16": "98838bc4dfe63493"},
+    # FETCH_SIZE 527749.0 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1081354336, "sources_sha256_16": "de4a6d1d99b16a7b"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
@@ -99,7 +99,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-long", action="store_true", help="skip the 32k long-context prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["prefill", "decode", "paged", "long", "chunk", "swa", "mqa", "all"],
+    ap.add_argument("--only", choices=["prefill", "decode", "mha", "paged", "long", "chunk", "swa", "mqa", "all"],
                     default="all")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for the HBM byte counters)")
@@ -327,7 +327,7 @@ def main():
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
-    if args.only == "all":
+    if args.only in ("mha", "all"):
         res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False)
     if args.only in ("swa", "all"):
         res["swa"] = bench_prefill(lib, inputs, W["swa"], max(5, args.steps // 2), max(3, args.warmup // 2),
