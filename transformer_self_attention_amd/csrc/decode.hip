@@ -77,9 +77,10 @@ __device__ __forceinline__ int vswz(int r, int lc) {  // 16 chunks per row (D = 
 // NW waves per workgroup.  WHOLE: one split covers the whole cache, and the workgroup writes the
 // final o (OUT_BF16 selects its type) and lse itself; otherwise it writes one partial (m, l, O)
 // per (row, split) for decode_merge_kernel.
-// STREAM: K/V are read once (nontemporal loads); off when several workgroups share a KV head
-// (more than 16 query heads per KV head), whose repeated reads should stay in L2.
-template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16, bool PAGED, bool STREAM>
+// STREAM: one workgroup per (sequence, KV head, split), and K/V read once (nontemporal loads);
+// off when several workgroups share a KV head (more than 16 query heads per KV head): their ids
+// are then placed on one XCD and their repeated reads should stay in L2.  WIN: sliding window.
+template <int D, bool ROPE, int NW, bool WHOLE, bool OUT_BF16, bool PAGED, bool STREAM, bool WIN>
 __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int B, int Hq, int Hkv,
@@ -99,18 +100,27 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t v_lds[kWaves][kSub * D];
   __shared__ float red_ml[kWaves][16][2];
 
-  // workgroup id -> (unit, sub-group): the n_sub workgroups of a unit share id % 8 (one XCD)
   const int G = Hq / Hkv;
-  const int n_sub = (G + 15) / 16;               // groups of 16 query heads per KV head
-  const int n_units = n_split * Hkv * B;
-  const int wid = blockIdx.x;
-  const int jx = wid / kNumXcd;
-  const int sub = jx % n_sub;
-  const int unit = (jx / n_sub) * kNumXcd + wid % kNumXcd;
-  if (unit >= n_units) return;
-  const int split = unit % n_split;
-  const int hkv = (unit / n_split) % Hkv;
-  const int b = unit / (n_split * Hkv);
+  int split, hkv, b, sub;
+  if constexpr (STREAM) {
+    // grid (n_split, Hkv, B): one group of query heads per KV head
+    split = blockIdx.x;
+    hkv = blockIdx.y;
+    b = blockIdx.z;
+    sub = 0;
+  } else {
+    // workgroup id -> (unit, sub-group): the n_sub workgroups of a unit share id % 8 (one XCD)
+    const int n_sub = (G + 15) / 16;             // groups of 16 query heads per KV head
+    const int n_units = n_split * Hkv * B;
+    const int wid = blockIdx.x;
+    const int jx = wid / kNumXcd;
+    sub = jx % n_sub;
+    const int unit = (jx / n_sub) * kNumXcd + wid % kNumXcd;
+    if (unit >= n_units) return;
+    split = unit % n_split;
+    hkv = (unit / n_split) % Hkv;
+    b = unit / (n_split * Hkv);
+  }
   const int h0 = hkv * G + sub * 16;             // first query head of this workgroup
   const int Gs = min(16, G - sub * 16);          // query heads of this workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -120,7 +130,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   int L = cache_len[b];
   L = L < 0 ? 0 : (L > S_max ? S_max : L);
   // first visible row (sliding window); q_pos is given whenever a window is
-  const int wstart = window < kNoWindow ? max(q_pos[b] - window, 0) : 0;
+  const int wstart = WIN ? max(q_pos[b] - window, 0) : 0;
   const int kbeg = max(split * chunk, wstart & ~(kSub - 1));
   const int kend0 = min(split * chunk + chunk, L);
   // nothing visible in this split: empty range (then every sub-block processed below holds at
@@ -402,7 +412,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
   if (lse && d == 0) lse[(int64_t)b * Hq + h] = ls;
 }
 
-template <int D, bool ROPE, bool PAGED, bool STREAM>
+template <int D, bool ROPE, bool PAGED, bool STREAM, bool WIN>
 hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const uint16_t* q = (const uint16_t*)a.q;
   const uint16_t* kc = (const uint16_t*)a.k;
@@ -410,23 +420,24 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const float2* tab = reinterpret_cast<const float2*>(a.table);
   const int n_sub = (a.Hq / a.Hkv + 15) / 16;
   const int64_t n_units = (int64_t)a.n_split * a.Hkv * a.B;
-  const unsigned grid = (unsigned)(((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * n_sub);
+  const dim3 grid = STREAM ? dim3(a.n_split, a.Hkv, a.B)
+                           : dim3((unsigned)(((n_units + kNumXcd - 1) / kNumXcd) * kNumXcd * n_sub));
   if (a.n_split == 1) {
-    // one workgroup per (sequence, KV head) streams the whole cache and writes o itself
+    // one workgroup per (sequence, KV head, query group) streams the whole cache and writes o itself
     if (a.out_bf16)
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED, STREAM>), dim3(grid),
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, true, PAGED, STREAM, WIN>), grid,
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
                          a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     else
-      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED, STREAM>), dim3(grid),
+      hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesWhole, true, false, PAGED, STREAM, WIN>), grid,
                          dim3(64 * kWavesWhole), 0, st, q, kc, vc, a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max,
                          tab, a.table_max_pos, 1, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table,
                          a.max_blocks, a.bs_log2, a.num_blocks, a.window);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED, STREAM>),
-                     dim3(grid), dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
+  hipLaunchKernelGGL((decode_split_kernel<D, ROPE, kWavesSplit, false, false, PAGED, STREAM, WIN>),
+                     grid, dim3(64 * kWavesSplit), 0, st, q, kc, vc, a.cache_len, a.q_pos,
                      a.B, a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse,
                      a.block_table, a.max_blocks, a.bs_log2, a.num_blocks, a.window);
   hipError_t e = hipGetLastError();
@@ -440,19 +451,24 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool PAGED, bool STREAM>
+template <bool PAGED, bool STREAM, bool WIN>
 hipError_t go_d(const DecodeArgs& a, hipStream_t st) {
   const bool rope = a.table != nullptr;
-  if (a.D == 64) return rope ? go<64, true, PAGED, STREAM>(a, st) : go<64, false, PAGED, STREAM>(a, st);
-  return rope ? go<128, true, PAGED, STREAM>(a, st) : go<128, false, PAGED, STREAM>(a, st);
+  if (a.D == 64) return rope ? go<64, true, PAGED, STREAM, WIN>(a, st) : go<64, false, PAGED, STREAM, WIN>(a, st);
+  return rope ? go<128, true, PAGED, STREAM, WIN>(a, st) : go<128, false, PAGED, STREAM, WIN>(a, st);
+}
+
+template <bool PAGED>
+hipError_t go_w(const DecodeArgs& a, hipStream_t st) {
+  const bool stream = a.Hq / a.Hkv <= 16;
+  if (a.window < kNoWindow) return stream ? go_d<PAGED, true, true>(a, st) : go_d<PAGED, false, true>(a, st);
+  return stream ? go_d<PAGED, true, false>(a, st) : go_d<PAGED, false, false>(a, st);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  const bool stream = a.Hq / a.Hkv <= 16;
-  if (a.block_table) return stream ? go_d<true, true>(a, st) : go_d<true, false>(a, st);
-  return stream ? go_d<false, true>(a, st) : go_d<false, false>(a, st);
+  return a.block_table ? go_w<true>(a, st) : go_w<false>(a, st);
 }
 
 }  // namespace attn
