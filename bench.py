@@ -205,6 +205,16 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
 
 
+def reference_gemm_tflops(n=8192, iters=20):
+    """torch.matmul bf16 n x n x n on the same GPU, timed like the prefill: what the vendor GEMM
+    reaches under this part's power limit (context for the prefill's fraction of peak)."""
+    import torch
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = time_calls(lambda: a @ b, iters, 5)
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def bench_paged_decode(lib, inputs, wl, steps, warmup, block_size=16):
     import torch
     log(f"[bench] generating paged decode inputs B={wl.B} cache={wl.S} block={block_size}")
@@ -328,6 +338,8 @@ def main():
         del src, dst
     if args.only in ("prefill", "all"):
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
+        res["gemm_tflops"] = reference_gemm_tflops()
+        log(f"[bench] reference: torch bf16 GEMM 8192^3 {res['gemm_tflops']:.1f} TFLOP/s")
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("mha", "all"):
@@ -368,6 +380,9 @@ def main():
             "config": {"workload": "GQA causal prefill with RoPE on Q and K", "B": wl.B, "Hq": wl.Hq,
                        "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D, "causal": True,
                        "rope_base": wl.rope_base, "flops_per_step": wl.prefill_flops()},
+            "context": {"torch_bf16_gemm_8192_tflops": round(res["gemm_tflops"], 1),
+                        "note": "the vendor GEMM on the same GPU in the same run: what plain bf16 matrix "
+                                "work reaches under this part's power limit"},
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated fp16 keys)",
                          "achieved": round(kt, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(kt / MFMA_BF16_PEAK_TFLOPS, 4),
