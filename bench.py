@@ -62,8 +62,8 @@ MEASURED_TRAFFIC = {
     # FETCH_SIZE 158235.2 KiB, WRITE_SIZE 131081.8 KiB per dispatch.
     "prefill_gqa": {"bytes_per_launch": 458293452, "sources_sha256_16": "49fb1668ac2746b5"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
-    # FETCH_SIZE 527749.0 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1081354336, "sources_sha256_16": "de4a6d1d99b16a7b"},
+    # FETCH_SIZE 528507.2 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1082907088, "sources_sha256_16": "4f99ebb01968b160"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
