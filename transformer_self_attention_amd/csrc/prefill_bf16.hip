@@ -124,34 +124,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // ---- Q fragments (B operand) ----
   typedef typename std::conditional<QK_BF16, bf16x8, f16x8>::type qk_t;
   qk_t qf[KS];
-  {
-    const int rc = row < Sq ? row : Sq - 1;
-    const uint16_t* qrow = q + (((int64_t)b * Hq + h) * Sq + rc) * D;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int d0 = 16 * ks + 8 * hl;
-      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (QK_BF16) {
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
-      } else {
-        float x[8];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
-        const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + rc) * (D / 2) + d0 / 2);
-        const f32x4 c01 = tp[0], c23 = tp[1];
-        const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          const float c = cs[2 * p], s = cs[2 * p + 1];
-          const float x0 = x[2 * p], x1 = x[2 * p + 1];
-          x[2 * p] = x0 * c - x1 * s;
-          x[2 * p + 1] = x0 * s + x1 * c;
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
-      }
-    }
-  }
 
   // ---- key range ----
   // Query row i sees key j when i + coff - window <= j <= i + coff (coff = 0: the square mask;
@@ -464,8 +436,39 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     if (t + 1 < n_tiles) fused_issue(k0 + kBN);
   };
 
+  // The first tile's loads go out before the Q rows are read and rotated, so the two latencies
+  // overlap at the start of every workgroup.
   issue_tile(t_first * kBN, k_lds0, v_lds0);
   fused_issue(t_first * kBN);
+  {
+    const int rc = row < Sq ? row : Sq - 1;
+    const uint16_t* qrow = q + (((int64_t)b * Hq + h) * Sq + rc) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 16 * ks + 8 * hl;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
+      if constexpr (QK_BF16) {
+        qf[ks] = __builtin_bit_cast(bf16x8, w);
+      } else {
+        float x[8];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
+        const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + rc) * (D / 2) + d0 / 2);
+        const f32x4 c01 = tp[0], c23 = tp[1];
+        const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float c = cs[2 * p], s = cs[2 * p + 1];
+          const float x0 = x[2 * p], x1 = x[2 * p + 1];
+          x[2 * p] = x0 * c - x1 * s;
+          x[2 * p + 1] = x0 * s + x1 * c;
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
+      }
+    }
+  }
+
   for (int t = t_first; t < n_tiles; t += 2) {
     tile_step(std::integral_constant<int, 0>{}, t);
     if (t + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
