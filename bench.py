@@ -59,8 +59,8 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 158235.2 KiB, WRITE_SIZE 131081.8 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 458293452, "sources_sha256_16": "49fb1668ac2746b5"},
+    # FETCH_SIZE 160646.8 KiB, WRITE_SIZE 131072.1 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 463222392, "sources_sha256_16": "95891e56fb39f0d7"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
     # FETCH_SIZE 528507.2 KiB, WRITE_SIZE 512.0 KiB per step.
     "decode": {"bytes_per_launch": 1082907088, "sources_sha256_16": "4f99ebb01968b160"},
