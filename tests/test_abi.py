@@ -171,9 +171,14 @@ def test_decode_workspace_geometry():
     assert lib.decode_num_splits(1, 8, 1, 40, 64, 8) == 2
     assert lib.decode_num_splits(1, 8, 1, 1, 64, 0) == 1
     assert lib.decode_workspace_bytes(0, 8, 1, 100, 64, 0) == 0
-    # more than 16 query heads per KV head: groups of 16 count as units
-    assert lib.decode_num_splits(32, 64, 1, 8192, 128, 0) == 4    # 32 x 4 units x 4 splits = 512
-    assert lib.decode_num_splits(64, 64, 1, 8192, 128, 0) == 1    # 256 units
+    # more than 16 query heads per KV head: one workgroup (128 KiB of LDS, one per CU) covers up
+    # to 64 query heads of a KV head; aim for 256 of them
+    assert lib.decode_num_splits(32, 64, 1, 8192, 128, 0) == 8    # 32 units x 8 splits = 256
+    assert lib.decode_num_splits(64, 64, 1, 8192, 128, 0) == 4
+    assert lib.decode_num_splits(256, 64, 1, 8192, 128, 0) == 1   # 256 units
+    assert lib.decode_num_splits(32, 128, 1, 8192, 128, 0) == 4   # two 64-head workgroups per unit
+    assert lib.decode_num_splits(32, 64, 2, 8192, 128, 0) == 4    # 32 heads per KV head: 64 units
+    assert lib.decode_num_splits(1, 64, 1, 1000, 128, 0) == 3     # 3 splits of 384 keys (64-key chunks)
     assert lib.decode_num_splits(4, 64, 3, 100, 128, 0) == 0      # Hq not a multiple of Hkv
 
 

@@ -132,16 +132,13 @@ def test_decode_large_groups(lib, B, Hq, Hkv, S, lens, n_split):
     empty = lens <= 0
     assert np.all(np.isneginf(got_lse[empty]))
     assert err_stats(got_lse[~empty], ref_lse[~empty])[0] < 2e-2
-    # paged: the same cache in blocks, bit-identical
+    # paged: the same cache in blocks
     pd = inputs.make_paged_decode(wl, block_size=16, cache_len=lens, q_pos=lens + 3)
     op = lib.decode_paged(pd.q.torch("cuda"), pd.k_pages.torch("cuda"), pd.v_pages.torch("cuda"),
                           torch.from_numpy(pd.block_table).cuda(), torch.from_numpy(lens).cuda(),
                           torch.from_numpy(lens + 3).cuda(), tab, n_split=n_split, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    if S % 16 == 0:
-        assert torch.equal(op, o)
-    else:
-        assert_bf16_parity(to_np(op), ref, "paged o")
+    assert_bf16_parity(to_np(op), ref, "paged o")
 
 
 def test_mqa_decode_config(lib):

@@ -33,23 +33,33 @@ attn_status check_rope(const float* table, int table_max_pos, int pos0, int S) {
 // Decode split geometry: keys per split are a multiple of the 32-key wave block.  A unit is a
 // (sequence, KV head, group of up to 16 query heads) triple: one workgroup per unit and split.
 void decode_geometry(int B, int Hq, int Hkv, int S_max, int n_split_req, int* n_split, int* chunk) {
+  const int G = Hq / Hkv;
   int ns = n_split_req;
   if (ns <= 0) {
-    // With >= 256 units, one 8-wave workgroup per unit streams the whole
-    // cache and writes o directly (no merge pass).  Below that, split the cache over 4-wave
-    // workgroups, aiming for >= 512 of them (2 per CU) with >= 256 keys per split.  Measured on
-    // batch 32 x 8 KV heads x 8192 keys: one split, 158 us; 2 splits + merge, 165 us; 4, 168 us.
-    const int64_t units = (int64_t)B * Hkv * ((Hq / Hkv + 15) / 16);
-    int64_t want = units >= 256 ? 1 : (512 + units - 1) / units;
+    int64_t want;
+    if (G <= 16) {
+      // With >= 256 units, one 8-wave workgroup per unit streams the whole cache and writes o
+      // directly (no merge pass).  Below that, split the cache over 4-wave workgroups, aiming
+      // for >= 512 of them (2 per CU) with >= 256 keys per split.  Measured on batch 32 x 8 KV
+      // heads x 8192 keys: one split, 158 us; 2 splits + merge, 165 us; 4, 168 us.
+      const int64_t units = (int64_t)B * Hkv;
+      want = units >= 256 ? 1 : (512 + units - 1) / units;
+    } else {
+      // Wide groups: one workgroup per (sequence, KV head, up to 64 query heads) holds 128 KiB
+      // of LDS stages, so one runs per CU; aim for >= 256 of them.
+      const int hg = G <= 32 ? 2 : 4;
+      const int64_t units = (int64_t)B * Hkv * (((G + 15) / 16 + hg - 1) / hg);
+      want = units >= 256 ? 1 : (256 + units - 1) / units;
+    }
     int64_t cap = S_max / 256;
     if (cap < 1) cap = 1;
     if (want > cap) want = cap;
     if (want < 1) want = 1;
     ns = (int)want;
   }
+  const int align = G <= 16 ? 32 : 64;
   int c = (S_max + ns - 1) / ns;
-  c = ((c + 31) / 32) * 32;
-  if (c < 32) c = 32;
+  c = ((c + align - 1) / align) * align;
   // drop splits that would start past S_max
   int ns_eff = (S_max + c - 1) / c;
   if (ns_eff < 1) ns_eff = 1;

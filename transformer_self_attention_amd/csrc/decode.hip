@@ -442,13 +442,7 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
                      a.block_table, a.max_blocks, a.bs_log2, a.num_blocks, a.window);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (a.out_bf16)
-    hipLaunchKernelGGL((decode_merge_kernel<D, true, ROPE>), dim3(a.Hq, a.B), dim3(D), 0, st, a.ws_o,
-                       a.ws_ml, a.q_pos, a.table_max_pos, a.Hq, a.n_split, a.o, a.lse);
-  else
-    hipLaunchKernelGGL((decode_merge_kernel<D, false, ROPE>), dim3(a.Hq, a.B), dim3(D), 0, st, a.ws_o,
-                       a.ws_ml, a.q_pos, a.table_max_pos, a.Hq, a.n_split, a.o, a.lse);
-  return hipGetLastError();
+  return launch_decode_merge(a, st);
 }
 
 template <bool PAGED, bool STREAM, bool WIN>
@@ -468,7 +462,26 @@ hipError_t go_w(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  return a.block_table ? go_w<true>(a, st) : go_w<false>(a, st);
+  if (a.block_table) return go_w<true>(a, st);
+  // wide groups on a contiguous cache: the shared-tile kernel (its byte offsets within one
+  // sequence's cache are 32-bit, with room above them for the offsets that move no data)
+  if (a.Hq / a.Hkv > 16 && (int64_t)a.S_max * a.D * 2 <= ((int64_t)1 << 30)) return launch_decode_wide(a, st);
+  return go_w<false>(a, st);
+}
+
+hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st) {
+  const bool rope = a.table != nullptr;
+  auto go_m = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(a.Hq, a.B), dim3(a.D), 0, st, a.ws_o, a.ws_ml, a.q_pos, a.table_max_pos, a.Hq,
+                       a.n_split, a.o, a.lse);
+    return hipGetLastError();
+  };
+  if (a.D == 64) {
+    if (a.out_bf16) return rope ? go_m(decode_merge_kernel<64, true, true>) : go_m(decode_merge_kernel<64, true, false>);
+    return rope ? go_m(decode_merge_kernel<64, false, true>) : go_m(decode_merge_kernel<64, false, false>);
+  }
+  if (a.out_bf16) return rope ? go_m(decode_merge_kernel<128, true, true>) : go_m(decode_merge_kernel<128, true, false>);
+  return rope ? go_m(decode_merge_kernel<128, false, true>) : go_m(decode_merge_kernel<128, false, false>);
 }
 
 }  // namespace attn
