@@ -89,3 +89,45 @@ def test_decode_wide_split_counts(lib):
         o = lib.decode(*args, n_split=ns, out_dtype=torch.float32)
         torch.cuda.synchronize()
         assert_bf16_parity(to_np(o), ref, f"o (n_split={ns})")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S,bs,lens,n_split,W", [
+    (3, 64, 1, 1000, 16, [1000, 517, 0], 0, None),
+    (2, 48, 2, 2050, 32, [2050, 2049], 3, None),
+    (2, 64, 1, 4096, 64, [4096, 4000], 0, 700),
+    (3, 20, 1, 900, 128, [900, 130, 1], 2, 64),
+])
+def test_decode_wide_paged(lib, B, Hq, Hkv, S, bs, lens, n_split, W):
+    """The paged cache: blocks scattered over the pool; blocks wholly before every window are
+    released (NaN, table entries -1 or out of range).  Equal, bit for bit, to the contiguous
+    decode of the same cache."""
+    banner(f"wide decode paged B={B} Hq={Hq} Hkv={Hkv} S={S} bs={bs} lens={lens} n_split={n_split} W={W}")
+    wl = inputs.Workload("w", B=B, Hq=Hq, Hkv=Hkv, S=S, D=128, dtype="bf16", seed=7200 + bs + S, kind="decode")
+    lens = np.array(lens, np.int32)
+    pd = inputs.make_paged_decode(wl, block_size=bs, cache_len=lens, q_pos=lens)
+    kp, vp, bt = pd.k_pages.bits.copy(), pd.v_pages.bits.copy(), pd.block_table.copy()
+    if W is not None:
+        for b in range(B):
+            # only rows from the window start on are read
+            first_needed = max(int(lens[b]) - W, 0) // bs
+            for j in range(first_needed):
+                kp[bt[b, j]] = inputs.BF16_NAN_BITS
+                vp[bt[b, j]] = inputs.BF16_NAN_BITS
+                bt[b, j] = -1 if j % 2 else 10 ** 8
+    to_dev = lambda bits: torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).cuda()
+    tab = lib.make_rope_table(int(lens.max()) + 1, 128)
+    cl = torch.from_numpy(lens).cuda()
+    qp = torch.from_numpy(lens.copy()).cuda()
+    lse = torch.empty((B, Hq), dtype=torch.float32, device="cuda")
+    o = lib.decode_paged(pd.q.torch("cuda"), to_dev(kp), to_dev(vp), torch.from_numpy(bt).cuda(), cl, qp, tab,
+                         n_split=n_split, window=W, out_dtype=torch.float32, lse=lse)
+    d = pd.contiguous
+    lc = torch.empty_like(lse)
+    oc = lib.decode(d.q.torch("cuda"), d.k_cache.torch("cuda"), d.v_cache.torch("cuda"), cl, qp, tab,
+                    n_split=n_split, window=W, out_dtype=torch.float32, lse=lc)
+    torch.cuda.synchronize()
+    assert torch.equal(o, oc) and torch.equal(lse, lc), "paged and contiguous decode differ"
+    ref, ref_lse = oracle.decode(pd.q.f64(), d.k_cache.f32, d.v_cache.f32, lens, lens, window=W)
+    assert_bf16_parity(to_np(o), ref, "paged o")
+    empty = np.isneginf(ref_lse)
+    assert np.all(np.isneginf(to_np(lse)[empty]))

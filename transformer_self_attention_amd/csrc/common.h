@@ -136,7 +136,9 @@ struct DecodeArgs {
 constexpr int kNoWindow = 1 << 30;
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st);
-// More than 16 query heads per KV head (contiguous cache): K/V tiles shared through LDS.
+// More than 16 query heads per KV head: K/V tiles shared through LDS.  Usable when
+// decode_wide_fits(a): the cache of one sequence (contiguous) or the pool (paged) is under 2 GiB.
+bool decode_wide_fits(const DecodeArgs& a);
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t st);
 // The merge pass over a.n_split partials in a.ws_o / a.ws_ml.
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st);

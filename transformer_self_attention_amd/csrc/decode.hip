@@ -462,11 +462,9 @@ hipError_t go_w(const DecodeArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
-  if (a.block_table) return go_w<true>(a, st);
-  // wide groups on a contiguous cache: the shared-tile kernel (its byte offsets within one
-  // sequence's cache are 32-bit, with room above them for the offsets that move no data)
-  if (a.Hq / a.Hkv > 16 && (int64_t)a.S_max * a.D * 2 <= ((int64_t)1 << 30)) return launch_decode_wide(a, st);
-  return go_w<false>(a, st);
+  // more than 16 query heads per KV head: the shared-tile kernel (its byte offsets are 32-bit)
+  if (decode_wide_fits(a)) return launch_decode_wide(a, st);
+  return a.block_table ? go_w<true>(a, st) : go_w<false>(a, st);
 }
 
 hipError_t launch_decode_merge(const DecodeArgs& a, hipStream_t st) {

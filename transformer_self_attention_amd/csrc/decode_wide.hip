@@ -21,6 +21,9 @@
 //    read through ds_read_b64_tr_b16: the same arithmetic as the narrow decode kernel.
 //  * Rows outside [window start, cache length) inside a tile are loaded from the nearest visible
 //    row (finite data) and masked, so rows before the window are never read.
+//  * Paged cache (PAGED): the pool [num_blocks, Hkv, bs, D] and the per-sequence block table of
+//    codingpancake.com section 6.2.  A 64-key tile spans at most four blocks (bs >= 16); their ids
+//    are scalar loads made one tile ahead, and each lane picks the one holding its row.
 //  * The two key halves of a head group merge through LDS; the workgroup then writes o and lse
 //    (one split) or one partial per (row, split) for the merge pass.
 #include "common.h"
@@ -36,7 +39,10 @@ constexpr int kStages = 4;
 constexpr int kNumXcd = 8;      // workgroup ids are dealt to the XCDs in turn
 constexpr float kRescaleThreshold = 8.0f;
 constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: 32-bit data format, raw
-constexpr int kDeadOffset = 0x7FFFFFF0;   // beyond any resource range: the load moves no data
+// Added to the byte offset of a load past the last tile: beyond any resource range (the ranges are
+// under 2^31 - 256 bytes, so the sum neither wraps nor lands inside), so the load moves no data.
+constexpr uint32_t kDeadOffset = 0x80000000u;
+constexpr int64_t kMaxWideBytes = ((int64_t)1 << 31) - 256;
 // Cache policy of the tile loads: nontemporal (each K/V byte is read once).  Measured against
 // the default policy: the same at 16 tiles per workgroup, 5.6 -> 6.5 TB/s at 64.
 constexpr int kLoadAux = 2;
@@ -81,13 +87,13 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-template <int D, bool ROPE, int HG, bool WHOLE, bool OUT_BF16, bool WIN>
+template <int D, bool ROPE, int HG, bool WHOLE, bool OUT_BF16, bool PAGED, bool WIN>
 __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ cache_len, const int32_t* __restrict__ q_pos, int B, int Hq, int Hkv,
     int S_max, const float2* __restrict__ table, int table_max_pos, int n_split, int chunk,
     float* __restrict__ ws_o, float* __restrict__ ws_ml, void* __restrict__ o, float* __restrict__ lse,
-    int window) {
+    const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks, int window) {
   constexpr int NW = 2 * HG;
   constexpr int NCH = D / 8;                    // 16-byte chunks per row
   constexpr int KS = D / 32;                    // MFMA k-steps over D
@@ -151,8 +157,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   // KV head)'s rows.  Every step issues one tile's loads, also past the last tile: those get an
   // offset beyond the resource's range, so they move no data and only keep the count of loads
   // in flight the same on every path (each wait below is then a fixed vmcnt). ----
-  const int64_t kv_off = ((int64_t)b * Hkv + hkv) * S_max * D;
-  const uint32_t kv_bytes = (uint32_t)S_max * D * 2;
+  // contiguous: this (sequence, KV head)'s rows; paged: the whole pool
+  const int64_t kv_off = PAGED ? 0 : ((int64_t)b * Hkv + hkv) * S_max * D;
+  const uint32_t kv_bytes = PAGED ? (uint32_t)num_blocks * Hkv * (D << bs_log2) * 2 : (uint32_t)S_max * D * 2;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kc + kv_off), (short)0, kv_bytes, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
@@ -164,19 +171,42 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
     dma_row[i] = C / NCH;
     dma_elem[i] = swz<D>(C / NCH, C % NCH) * 8;
   }
-  auto issue = [&](int t, uint16_t* stage, uint16_t* vstage) {
+  // Paged: ids of the (up to four) blocks holding the visible rows of tile t, as wave-uniform
+  // scalar loads (their indices are clamped into the table row; the ids are clamped into the
+  // pool only where they are used, so the four loads are in flight together).
+  const int32_t* btr = block_table + (PAGED ? (int64_t)b * max_blocks : 0);
+  const int jmax = max(kend - 1, 0) >> bs_log2;
+  auto tile_blocks = [&](int t, int (&ids)[4]) {
+    if constexpr (PAGED) {
+      const int k0c = max(min(max(kbeg + t * kTileKeys, wstart), kend - 1), 0);
+      const int j0 = wave_uniform(k0c >> bs_log2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ids[i] = btr[min(j0 + i, jmax)];  // clamped where used
+    }
+  };
+  auto issue = [&](int t, uint16_t* stage, uint16_t* vstage, const int (&ids)[4]) {
     const int k0 = kbeg + t * kTileKeys;
-    // 0 for a tile to load, kDeadOffset past the last tile (an OR, not a branch, so that every
+    // 0 for a tile to load, kDeadOffset past the last tile (an add, not a branch, so that every
     // path issues the same loads)
-    const int dead = (t < nt) ? 0 : kDeadOffset;
+    const uint32_t dead = (t < nt) ? 0u : kDeadOffset;
+    const int j0 = max(min(max(k0, wstart), kend - 1), 0) >> bs_log2;
 #pragma unroll
     for (int i = 0; i < LPW; ++i) {
       const int key = max(min(max(k0 + dma_row[i], wstart), kend - 1), 0);
-      const int off = ((key * D + dma_elem[i]) * 2) | dead;
+      uint32_t row;
+      if constexpr (PAGED) {
+        const int jj = (key >> bs_log2) - j0;  // 0 .. 3
+        int blk = jj == 0 ? ids[0] : jj == 1 ? ids[1] : jj == 2 ? ids[2] : ids[3];
+        blk = min(max(blk, 0), num_blocks - 1);
+        row = ((uint32_t)(blk * Hkv + hkv) << bs_log2) + (uint32_t)(key & ((1 << bs_log2) - 1));
+      } else {
+        row = (uint32_t)key;
+      }
+      const uint32_t off = (row * D + dma_elem[i]) * 2 + dead;
       ATTN_LDS void* lk = (ATTN_LDS void*)(stage + (i * NW + wave) * 512);
       ATTN_LDS void* lv = (ATTN_LDS void*)(vstage + (i * NW + wave) * 512);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lk, 16, off, 0, 0, kLoadAux);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lv, 16, off, 0, 0, kLoadAux);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lk, 16, (int)off, 0, 0, kLoadAux);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lv, 16, (int)off, 0, 0, kLoadAux);
     }
   };
   auto stage_of = [&](auto s_c) -> uint16_t* {
@@ -219,10 +249,16 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
       }
     }
   }
-  issue(0, st0, sv0);
-  if constexpr (kStages > 2) issue(1, st1, sv1);
-  if constexpr (kStages > 3) issue(2, st2, sv2);
-  if constexpr (kStages > 4) issue(3, st3, sv3);
+  int ids_a[4] = {0, 0, 0, 0}, ids_b[4] = {0, 0, 0, 0}, ids_c[4] = {0, 0, 0, 0};
+  tile_blocks(0, ids_a);
+  if constexpr (kStages > 2) tile_blocks(1, ids_b);
+  if constexpr (kStages > 3) tile_blocks(2, ids_c);
+  issue(0, st0, sv0, ids_a);
+  if constexpr (kStages > 2) issue(1, st1, sv1, ids_b);
+  if constexpr (kStages > 3) issue(2, st2, sv2, ids_c);
+  if constexpr (kStages > 4) { tile_blocks(3, ids_a); issue(3, st3, sv3, ids_a); }
+  int nid[4] = {0, 0, 0, 0};  // paged: blocks of the next tile to issue
+  tile_blocks(kStages - 1, nid);
   bf16x8 qhi[KS], qlo[KS];
   {
     const float qscale = 1.4426950408889634f / sqrtf((float)D);
@@ -351,8 +387,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((P - 1) * LPT));
     lds_barrier();
     issue(t + P, stage_of(std::integral_constant<int, (S + P) % kStages>{}),
-          vstage_of(std::integral_constant<int, (S + P) % kStages>{}));
+          vstage_of(std::integral_constant<int, (S + P) % kStages>{}), nid);
     compute(stage_of(s_c), vstage_of(s_c), t);
+    tile_blocks(t + P + 1, nid);  // paged: their latency passes during the next wait
   };
   for (int t = 0; t < nt; t += kStages) {
     step(std::integral_constant<int, 0>{}, t);
@@ -436,7 +473,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   }
 }
 
-template <int D, bool ROPE, int HG, bool WIN>
+template <int D, bool ROPE, int HG, bool PAGED, bool WIN>
 hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const int n_sub = (a.Hq / a.Hkv + 15) / 16;
   const int n_super = (n_sub + HG - 1) / HG;
@@ -447,39 +484,47 @@ hipError_t go(const DecodeArgs& a, hipStream_t st) {
   const uint16_t* kc = (const uint16_t*)a.k;
   const uint16_t* vc = (const uint16_t*)a.v;
   const float2* tab = reinterpret_cast<const float2*>(a.table);
-  if (a.n_split == 1) {
-    if (a.out_bf16)
-      hipLaunchKernelGGL((decode_wide_kernel<D, ROPE, HG, true, true, WIN>), grid, block, 0, st, q, kc, vc,
-                         a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, 1, a.chunk,
-                         a.ws_o, a.ws_ml, a.o, a.lse, a.window);
-    else
-      hipLaunchKernelGGL((decode_wide_kernel<D, ROPE, HG, true, false, WIN>), grid, block, 0, st, q, kc, vc,
-                         a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, 1, a.chunk,
-                         a.ws_o, a.ws_ml, a.o, a.lse, a.window);
+  auto launch = [&](auto kernel, int n_split) {
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, q, kc, vc, a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max, tab,
+                       a.table_max_pos, n_split, a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.block_table, a.max_blocks,
+                       a.bs_log2, a.num_blocks, a.window);
     return hipGetLastError();
+  };
+  if (a.n_split == 1) {
+    return a.out_bf16 ? launch(decode_wide_kernel<D, ROPE, HG, true, true, PAGED, WIN>, 1)
+                      : launch(decode_wide_kernel<D, ROPE, HG, true, false, PAGED, WIN>, 1);
   }
-  hipLaunchKernelGGL((decode_wide_kernel<D, ROPE, HG, false, false, WIN>), grid, block, 0, st, q, kc, vc,
-                     a.cache_len, a.q_pos, a.B, a.Hq, a.Hkv, a.S_max, tab, a.table_max_pos, a.n_split,
-                     a.chunk, a.ws_o, a.ws_ml, a.o, a.lse, a.window);
-  const hipError_t e = hipGetLastError();
+  const hipError_t e = launch(decode_wide_kernel<D, ROPE, HG, false, false, PAGED, WIN>, a.n_split);
   if (e != hipSuccess) return e;
   return launch_decode_merge(a, st);
 }
 
-template <int D, bool ROPE>
+template <int D, bool ROPE, bool PAGED>
 hipError_t go_hg(const DecodeArgs& a, hipStream_t st) {
   const bool win = a.window < kNoWindow;
   if (a.Hq / a.Hkv <= 32)
-    return win ? go<D, ROPE, 2, true>(a, st) : go<D, ROPE, 2, false>(a, st);
-  return win ? go<D, ROPE, 4, true>(a, st) : go<D, ROPE, 4, false>(a, st);
+    return win ? go<D, ROPE, 2, PAGED, true>(a, st) : go<D, ROPE, 2, PAGED, false>(a, st);
+  return win ? go<D, ROPE, 4, PAGED, true>(a, st) : go<D, ROPE, 4, PAGED, false>(a, st);
+}
+
+template <bool PAGED>
+hipError_t go_d(const DecodeArgs& a, hipStream_t st) {
+  const bool rope = a.table != nullptr;
+  if (a.D == 64) return rope ? go_hg<64, true, PAGED>(a, st) : go_hg<64, false, PAGED>(a, st);
+  return rope ? go_hg<128, true, PAGED>(a, st) : go_hg<128, false, PAGED>(a, st);
 }
 
 }  // namespace
 
+bool decode_wide_fits(const DecodeArgs& a) {
+  if (a.Hq / a.Hkv <= 16) return false;
+  const int64_t bytes = a.block_table ? (int64_t)a.num_blocks * a.Hkv * ((int64_t)a.D << a.bs_log2) * 2
+                                      : (int64_t)a.S_max * a.D * 2;
+  return bytes <= kMaxWideBytes;
+}
+
 hipError_t launch_decode_wide(const DecodeArgs& a, hipStream_t st) {
-  const bool rope = a.table != nullptr;
-  if (a.D == 64) return rope ? go_hg<64, true>(a, st) : go_hg<64, false>(a, st);
-  return rope ? go_hg<128, true>(a, st) : go_hg<128, false>(a, st);
+  return a.block_table ? go_d<true>(a, st) : go_d<false>(a, st);
 }
 
 }  // namespace attn
