@@ -385,17 +385,35 @@ template <int D, bool OUT_BF16, bool ROPE>
 __global__ __launch_bounds__(D) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_ml, const int32_t* __restrict__ q_pos,
     int table_max_pos, int Hq, int n_split, void* __restrict__ o, float* __restrict__ lse) {
+  constexpr int kGroup = 8;  // partials whose loads are in flight together
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int64_t base = ((int64_t)b * Hq + h) * n_split;
-  float M = -INFINITY;
-  for (int s = 0; s < n_split; ++s) M = fmaxf(M, ws_ml[(base + s) * 2]);
-  float Lsum = 0.f, acc = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < n_split; ++s) {
-      const float sc = fast_exp2(ws_ml[(base + s) * 2] - M);
-      Lsum += ws_ml[(base + s) * 2 + 1] * sc;
-      acc += ws_o[(base + s) * D + d] * sc;
+  // One pass over the splits, kGroup at a time, rescaling the running sum to each group's max.
+  float M = -INFINITY, Lsum = 0.f, acc = 0.f;
+  for (int s0 = 0; s0 < n_split; s0 += kGroup) {
+    float m[kGroup], l[kGroup], x[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const bool in = s0 + i < n_split;
+      const int64_t part = base + (in ? s0 + i : 0);
+      m[i] = in ? ws_ml[part * 2] : -INFINITY;
+      l[i] = ws_ml[part * 2 + 1];
+      x[i] = ws_o[part * D + d];
     }
+    float Mg = M;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) Mg = fmaxf(Mg, m[i]);
+    if (Mg == -INFINITY) continue;  // nothing seen yet (empty splits)
+    const float r = fast_exp2(M - Mg);  // 0 while M is -inf
+    Lsum *= r;
+    acc *= r;
+#pragma unroll
+    for (int i = 0; i < kGroup; ++i) {
+      const float sc = fast_exp2(m[i] - Mg);  // 0 for empty splits and those past n_split
+      Lsum += l[i] * sc;
+      acc += x[i] * sc;
+    }
+    M = Mg;
   }
   float out = Lsum > 0.f ? acc / Lsum : 0.f;
   float ls = Lsum > 0.f ? (M + log2f(Lsum)) * 0.6931471805599453f : -INFINITY;
