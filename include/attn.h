@@ -228,8 +228,8 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
  * same B, Hq, Hkv, S_max, D and n_split; its contents on entry do not matter.
  *
  * Support matrix: in_dt = ATTN_BF16, D in {64, 128}, out_dt either; any group size Hq / Hkv
- * (query heads are taken 16 at a time per workgroup; with more than 16 per KV head, as in
- * multi-query attention, the groups of one KV head read its K/V back to back).
+ * (with more than 16 query heads per KV head, as in multi-query attention, a workgroup reads
+ * each K/V tile once for up to 64 of them).
  * Errors: ATTN_ERR_INVALID_ARG for null pointers (q_pos may be NULL only without RoPE and
  * without a window), sizes < 1, Hq % Hkv != 0, n_split < 0, workspace too small, misalignment;
  * ATTN_ERR_UNSUPPORTED outside the support matrix.
