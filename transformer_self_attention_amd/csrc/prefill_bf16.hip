@@ -499,34 +499,6 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 }
 
-// One pass over K: rotate every row at position pos0 + s (fp32 arithmetic, the same coefficient
-// table) and store it as fp16, the operand format of the Q.K^T product.
-template <int D>
-__global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restrict__ k,
-                                                         uint16_t* __restrict__ out, int64_t rows, int S,
-                                                         int pos0, const float2* __restrict__ table) {
-  constexpr int NCH = D / 8;
-  const int64_t n = rows * NCH;
-  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
-       idx += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t r = idx / NCH;
-    const int cc = (int)(idx - r * NCH);
-    const int pos = pos0 + (int)(r % S);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(k + r * D + cc * 8);
-    const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)pos * (D / 2) + cc * 4);
-    const f32x4 c01 = tp[0], c23 = tp[1];
-    const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-    u32x4 hw;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const float x0 = bf16lo(w[p]), x1 = bf16hi(w[p]);
-      const float c = cs[2 * p], s = cs[2 * p + 1];
-      hw[p] = pack_f16(x0 * c - x1 * s, x0 * s + x1 * c);
-    }
-    *reinterpret_cast<u32x4*>(out + r * D + cc * 8) = hw;
-  }
-}
-
 template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, bool WIN>
 hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   constexpr int NW = kWavesStream;
@@ -553,22 +525,11 @@ hipError_t dispatch_mode(const PrefillArgs& a, const void* kptr, hipStream_t st)
 }
 
 template <int D>
-hipError_t rotate_keys(const void* k, void* k_rot, int64_t rows, int S, int pos0, const float* table,
-                       hipStream_t st) {
-  int64_t blocks = (rows * (D / 8) + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(rope_k_f16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const uint16_t*)k, (uint16_t*)k_rot, rows, S, pos0,
-                     reinterpret_cast<const float2*>(table));
-  return hipGetLastError();
-}
-
-template <int D>
 hipError_t dispatch_d(const PrefillArgs& a, hipStream_t st) {
   if (!a.table) return dispatch_mode<D, KMODE_RAW>(a, a.k, st);
   if (!a.workspace) return dispatch_mode<D, KMODE_FUSED>(a, a.k, st);
   // one pass: rotated fp16 keys into the workspace, then the attention kernel streams them
-  const hipError_t e = rotate_keys<D>(a.k, a.workspace, (int64_t)a.B * a.Hkv * a.S, a.S, a.pos0, a.table, st);
+  const hipError_t e = launch_rotate_keys_f16(a.k, a.workspace, a.B, a.Hkv, a.S, D, a.pos0, a.table, st);
   if (e != hipSuccess) return e;
   return dispatch_mode<D, KMODE_PREROT>(a, a.workspace, st);
 }
@@ -581,13 +542,6 @@ size_t prefill_workspace_bytes(int B, int Hkv, int S, int D) {
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   return a.D == 64 ? dispatch_d<64>(a, st) : dispatch_d<128>(a, st);
-}
-
-hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
-                                  const float* table, hipStream_t st) {
-  const int64_t rows = (int64_t)B * Hkv * S;
-  return D == 64 ? rotate_keys<64>(k, k_rot, rows, S, pos0, table, st)
-                 : rotate_keys<128>(k, k_rot, rows, S, pos0, table, st);
 }
 
 hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hipStream_t st) {

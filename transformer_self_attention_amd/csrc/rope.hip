@@ -1,4 +1,5 @@
-// Rotary position embeddings: coefficient table and the stand-alone rotation kernel.
+// Rotary position embeddings: coefficient table, the stand-alone rotation kernel, and the key
+// rotation pass of the bf16 prefill (rotated keys stored as fp16).
 //
 // The rotation follows "Transformer Architecture & Self-Attention Mechanics" (devthesis.com),
 // section 3, "Rotary Position Embeddings (RoPE)": adjacent pairs (x[2i], x[2i+1]) of a head
@@ -154,6 +155,55 @@ hipError_t launch_rope_apply(const void* x, void* out, bool bf16, int64_t rows, 
   }
   if (half % 2 == 0) return rope_apply_go<false, 2>(x, out, rows, S, D, pos0, table, st);
   return rope_apply_go<false, 1>(x, out, rows, S, D, pos0, table, st);
+}
+
+
+// One pass over K: rotate every row at position pos0 + s (fp32 arithmetic, the same coefficient
+// table) and store it as fp16, the operand format of the Q.K^T product of the bf16 prefill.  K is
+// not read again, so its loads are nontemporal and leave the caches to the fp16 copy and V (a
+// whole MHA step at 2k tokens +1 to +5%).
+template <int D>
+__global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restrict__ k,
+                                                         uint16_t* __restrict__ out, int64_t rows, int S,
+                                                         int pos0, const float2* __restrict__ table) {
+  constexpr int NCH = D / 8;
+  const int64_t n = rows * NCH;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = idx / NCH;
+    const int cc = (int)(idx - r * NCH);
+    const int pos = pos0 + (int)(r % S);
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + r * D + cc * 8));
+    const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)pos * (D / 2) + cc * 4);
+    const f32x4 c01 = tp[0], c23 = tp[1];
+    const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+    u32x4 hw;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = bf16lo(w[p]), x1 = bf16hi(w[p]);
+      const float c = cs[2 * p], s = cs[2 * p + 1];
+      hw[p] = pack_f16(x0 * c - x1 * s, x0 * s + x1 * c);
+    }
+    *reinterpret_cast<u32x4*>(out + r * D + cc * 8) = hw;
+  }
+}
+
+template <int D>
+static hipError_t rotate_keys(const void* k, void* k_rot, int64_t rows, int S, int pos0, const float* table,
+                       hipStream_t st) {
+  int64_t blocks = (rows * (D / 8) + 255) / 256;
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(rope_k_f16_kernel<D>, dim3((unsigned)blocks), dim3(256), 0, st,
+                     (const uint16_t*)k, (uint16_t*)k_rot, rows, S, pos0,
+                     reinterpret_cast<const float2*>(table));
+  return hipGetLastError();
+}
+
+hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
+                                  const float* table, hipStream_t st) {
+  const int64_t rows = (int64_t)B * Hkv * S;
+  return D == 64 ? rotate_keys<64>(k, k_rot, rows, S, pos0, table, st)
+                 : rotate_keys<128>(k, k_rot, rows, S, pos0, table, st);
 }
 
 }  // namespace attn
