@@ -131,3 +131,54 @@ def test_decode_wide_paged(lib, B, Hq, Hkv, S, bs, lens, n_split, W):
     assert_bf16_parity(to_np(o), ref, "paged o")
     empty = np.isneginf(ref_lse)
     assert np.all(np.isneginf(to_np(lse)[empty]))
+
+
+def test_decode_wide_groups_cache_over_2gib(lib):
+    """A sequence's cache over 2 GiB (S_max > 2^23 rows at D = 128): the wide kernel's 32-bit
+    offsets do not reach, so the query heads go 16 per workgroup through the narrow kernel.  Only
+    the first cache_len rows hold data; the rest is never read (left as NaN)."""
+    B, Hq, Hkv, D, L = 2, 32, 1, 128, 2500
+    S_max = (1 << 23) + 256
+    banner(f"wide groups, cache over 2 GiB: B={B} Hq={Hq} Hkv={Hkv} S_max={S_max} L={L}")
+    wl = inputs.Workload("w", B=B, Hq=Hq, Hkv=Hkv, S=L, D=D, dtype="bf16", seed=7300, kind="decode")
+    lens = np.array([L, L - 777], np.int32)
+    d = inputs.make_decode(wl, cache_len=lens, q_pos=lens)
+    nan = torch.tensor(inputs.BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16).item()
+    kc = torch.full((B, Hkv, S_max, D), nan, dtype=torch.bfloat16, device="cuda")
+    vc = torch.full((B, Hkv, S_max, D), nan, dtype=torch.bfloat16, device="cuda")
+    for b in range(B):
+        kc[b, :, :lens[b]] = d.k_cache.torch("cuda")[b, :, :lens[b]]
+        vc[b, :, :lens[b]] = d.v_cache.torch("cuda")[b, :, :lens[b]]
+    tab = lib.make_rope_table(L + 1, D)
+    cl = torch.from_numpy(lens).cuda()
+    o = lib.decode(d.q.torch("cuda"), kc, vc, cl, cl.clone(), tab, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del kc, vc
+    ref, _ = oracle.decode(d.q.f64(), d.k_cache.f32, d.v_cache.f32, lens, lens)
+    assert_bf16_parity(to_np(o), ref, "o (cache over 2 GiB)")
+
+
+def test_decode_wide_groups_pool_over_2gib(lib):
+    """A paged pool over 2 GiB with the sequences' blocks at its far end (byte offsets past
+    2^31): the narrow kernel again, with 64-bit addresses.  Equal to the contiguous decode."""
+    B, Hq, Hkv, S, D, bs = 2, 64, 1, 1000, 128, 16
+    banner(f"wide groups, pool over 2 GiB: B={B} Hq={Hq} Hkv={Hkv} S={S} bs={bs}")
+    wl = inputs.Workload("w", B=B, Hq=Hq, Hkv=Hkv, S=S, D=D, dtype="bf16", seed=7400, kind="decode")
+    lens = np.array([S, 321], np.int32)
+    pd = inputs.make_paged_decode(wl, block_size=bs, cache_len=lens, q_pos=lens)
+    n_small = pd.k_pages.shape[0]
+    n_big = (1 << 31) // (Hkv * bs * D * 2) + 4096            # 2 GiB + 16 MiB per pool
+    off = n_big - n_small                                     # the used blocks at the end
+    nan = torch.tensor(inputs.BF16_NAN_BITS, dtype=torch.int16).view(torch.bfloat16).item()
+    kp = torch.full((n_big, Hkv, bs, D), nan, dtype=torch.bfloat16, device="cuda")
+    vp = torch.full((n_big, Hkv, bs, D), nan, dtype=torch.bfloat16, device="cuda")
+    kp[off:] = pd.k_pages.torch("cuda")
+    vp[off:] = pd.v_pages.torch("cuda")
+    bt = torch.from_numpy(pd.block_table + off).cuda()
+    tab = lib.make_rope_table(S + 1, D)
+    cl = torch.from_numpy(lens).cuda()
+    o = lib.decode_paged(pd.q.torch("cuda"), kp, vp, bt, cl, cl.clone(), tab, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    del kp, vp
+    ref, _ = oracle.decode(pd.q.f64(), pd.contiguous.k_cache.f32, pd.contiguous.v_cache.f32, lens, lens)
+    assert_bf16_parity(to_np(o), ref, "paged o (pool over 2 GiB)")
