@@ -11,7 +11,7 @@
 // query heads), NW = 2 * HG waves:
 //  * Wave w owns the 16 query heads of head group w % HG (the 16 columns of the MFMA B operand)
 //    and the 32-key half w / HG of every 64-key tile.
-//  * The K and V tiles go HBM -> LDS once per workgroup (global_load_lds_dwordx4, no register
+//  * The K and V tiles go HBM -> LDS once per workgroup (buffer_load_dwordx4 ... lds, no register
 //    staging), into kStages stages with kStages - 1 tiles in flight, and all HG head groups read
 //    their MFMA operands from there: every K/V byte leaves HBM once for up to HG x 16 query
 //    heads.  (The decode kernel for G <= 16 instead loads K straight into registers, one query
@@ -43,8 +43,8 @@ constexpr int kBufferWord3 = 0x00020000;  // buffer resource word 3: 32-bit data
 // under 2^31 - 256 bytes, so the sum neither wraps nor lands inside), so the load moves no data.
 constexpr uint32_t kDeadOffset = 0x80000000u;
 constexpr int64_t kMaxWideBytes = ((int64_t)1 << 31) - 256;
-// Cache policy of the tile loads: nontemporal (each K/V byte is read once).  Measured against
-// the default policy: the same at 16 tiles per workgroup, 5.6 -> 6.5 TB/s at 64.
+// Cache policy of the tile loads: the nontemporal bit (each K/V byte is read once).  Measured
+// against the default policy: the same at 16 tiles per workgroup, 5.6 -> 6.5 TB/s at 64.
 constexpr int kLoadAux = 2;
 
 // s_waitcnt with only vmcnt limited (expcnt 7, lgkmcnt 15): vmcnt sits in bits 3:0 and 15:14.
@@ -109,15 +109,13 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   // compiler sees that loads into the other stages never alias the operands being read.
   __shared__ __attribute__((aligned(16))) uint16_t st0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t st1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t st2[kStages > 2 ? TILE : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t st3[kStages > 3 ? TILE : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t st4[kStages > 4 ? TILE : 1];
+  __shared__ __attribute__((aligned(16))) uint16_t st2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t st3[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sv0[TILE];
   __shared__ __attribute__((aligned(16))) uint16_t sv1[TILE];
-  __shared__ __attribute__((aligned(16))) uint16_t sv2[kStages > 2 ? TILE : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sv3[kStages > 3 ? TILE : 1];
-  __shared__ __attribute__((aligned(16))) uint16_t sv4[kStages > 4 ? TILE : 1];
-  static_assert(kStages >= 2 && kStages <= 5, "two to five stage objects");
+  __shared__ __attribute__((aligned(16))) uint16_t sv2[TILE];
+  __shared__ __attribute__((aligned(16))) uint16_t sv3[TILE];
+  static_assert(kStages == 4, "four stage objects per tensor");
   static_assert(2 * 16 * D * 4 <= TILE * 2, "two head groups' partial O fit in one K stage");
 
   // ---- workgroup -> (unit, super-group); the super-groups of a unit share an XCD ----
@@ -214,16 +212,14 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
     if constexpr (S == 0) return st0;
     else if constexpr (S == 1) return st1;
     else if constexpr (S == 2) return st2;
-    else if constexpr (S == 3) return st3;
-    else return st4;
+    else return st3;
   };
   auto vstage_of = [&](auto s_c) -> uint16_t* {
     constexpr int S = decltype(s_c)::value;
     if constexpr (S == 0) return sv0;
     else if constexpr (S == 1) return sv1;
     else if constexpr (S == 2) return sv2;
-    else if constexpr (S == 3) return sv3;
-    else return sv4;
+    else return sv3;
   };
 
   // ---- query fragments (hi/lo bf16), rotated at q_pos[b] and scaled by log2(e)/sqrt(D); the
@@ -251,12 +247,11 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   }
   int ids_a[4] = {0, 0, 0, 0}, ids_b[4] = {0, 0, 0, 0}, ids_c[4] = {0, 0, 0, 0};
   tile_blocks(0, ids_a);
-  if constexpr (kStages > 2) tile_blocks(1, ids_b);
-  if constexpr (kStages > 3) tile_blocks(2, ids_c);
+  tile_blocks(1, ids_b);
+  tile_blocks(2, ids_c);
   issue(0, st0, sv0, ids_a);
-  if constexpr (kStages > 2) issue(1, st1, sv1, ids_b);
-  if constexpr (kStages > 3) issue(2, st2, sv2, ids_c);
-  if constexpr (kStages > 4) { tile_blocks(3, ids_a); issue(3, st3, sv3, ids_a); }
+  issue(1, st1, sv1, ids_b);
+  issue(2, st2, sv2, ids_c);
   int nid[4] = {0, 0, 0, 0};  // paged: blocks of the next tile to issue
   tile_blocks(kStages - 1, nid);
   bf16x8 qhi[KS], qlo[KS];
@@ -377,11 +372,11 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
     }
   };
 
-  // Tile t sits in stage t % 5.  Before it is read, each wave waits for its own loads of it
-  // (vmcnt counts this wave's loads in issue order; the three tiles issued after t may stay in
+  // Tile t sits in stage t % 4.  Before it is read, each wave waits for its own loads of it
+  // (vmcnt counts this wave's loads in issue order; the two tiles issued after t may stay in
   // flight), then the barrier publishes every wave's part and guarantees every wave is done
-  // with tile t - 1, whose stage the loads of tile t + 4 then reuse.  Steps past the last tile
-  // (to a multiple of five) only wait, meet the barrier and issue loads that move no data.
+  // with tile t - 1, whose stage the loads of tile t + 3 then reuse.  Steps past the last tile
+  // (to a multiple of four) only wait, meet the barrier and issue loads that move no data.
   auto step = [&](auto s_c, int t) {
     constexpr int S = decltype(s_c)::value;
     __builtin_amdgcn_s_waitcnt(waitcnt_vm((P - 1) * LPT));
@@ -394,9 +389,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   for (int t = 0; t < nt; t += kStages) {
     step(std::integral_constant<int, 0>{}, t);
     step(std::integral_constant<int, 1>{}, t + 1);
-    if constexpr (kStages > 2) step(std::integral_constant<int, 2>{}, t + 2);
-    if constexpr (kStages > 3) step(std::integral_constant<int, 3>{}, t + 3);
-    if constexpr (kStages > 4) step(std::integral_constant<int, 4>{}, t + 4);
+    step(std::integral_constant<int, 2>{}, t + 2);
+    step(std::integral_constant<int, 3>{}, t + 3);
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // the loads past the end may still write LDS
 
