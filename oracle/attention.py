@@ -364,3 +364,51 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, *, rope_bas
             kc[b, :, t] = kp[blk, :, t % bs]
             vc[b, :, t] = vp[blk, :, t % bs]
     return decode(q, kc, vc, cache_len, q_pos, rope_base=rope_base, window=window, rope_scaling=rope_scaling)
+
+
+def append_to_cache_paged(k_pages, v_pages, block_table, k_new, v_new, pos0: int, *, rope_base=10000.0,
+                          rope_scaling=None):
+    """Pools after a chunk of Sq new tokens of every sequence is written into its blocks.
+
+    k_pages, v_pages: [num_blocks, Hkv, block_size, D]; block_table: int [B, max_blocks] (token t
+    of sequence b lives in block block_table[b, t // block_size], slot t % block_size,
+    codingpancake.com section 6.2); k_new, v_new: [B, Hkv, Sq, D].  Token pos0 + i gets key row
+    i rotated at position pos0 + i (unless rope_base is None) and rounded to bfloat16, and value
+    row i as given.  Every other slot is unchanged.  Returns new arrays.
+    """
+    kp = np.array(k_pages, dtype=np.float64, copy=True)
+    vp = np.array(v_pages, dtype=np.float64, copy=True)
+    bt = np.asarray(block_table)
+    k_new = np.asarray(k_new, dtype=np.float64)
+    v_new = np.asarray(v_new, dtype=np.float64)
+    B, _, Sq, _ = k_new.shape
+    bs = kp.shape[2]
+    if pos0 < 0 or pos0 + Sq > bt.shape[1] * bs:
+        raise ValueError("chunk does not fit the block table")
+    kr = rope(k_new, pos0 + np.arange(Sq), rope_base, rope_scaling) if rope_base is not None else k_new
+    kr = round_bf16(kr)
+    for b in range(B):
+        for i in range(Sq):
+            t = pos0 + i
+            blk = int(bt[b, t // bs])
+            kp[blk, :, t % bs] = kr[b, :, i]
+            vp[blk, :, t % bs] = v_new[b, :, i]
+    return kp, vp
+
+
+def gather_pages(k_pages, v_pages, block_table, n_tokens: int):
+    """The first n_tokens tokens of every sequence of a paged cache as contiguous arrays
+    [B, Hkv, n_tokens, D] (same placement rule as append_to_cache_paged)."""
+    kp = np.asarray(k_pages, dtype=np.float64)
+    vp = np.asarray(v_pages, dtype=np.float64)
+    bt = np.asarray(block_table)
+    B = bt.shape[0]
+    _, Hkv, bs, D = kp.shape
+    kc = np.empty((B, Hkv, n_tokens, D))
+    vc = np.empty((B, Hkv, n_tokens, D))
+    for b in range(B):
+        for t in range(n_tokens):
+            blk = int(bt[b, t // bs])
+            kc[b, :, t] = kp[blk, :, t % bs]
+            vc[b, :, t] = vp[blk, :, t % bs]
+    return kc, vc

@@ -7,7 +7,8 @@ Passages: the KV cache of "Transformer internals: attention without the mysticis
 stored and reused); chunked prefill as named on "Multi-Head Attention & Rotary Position
 Embeddings (RoPE)" (learnllm.online), "Prefill vs Decode Latency & Memory Wall Waterfall"; the
 causal mask of the same page's PyTorch listing; the paged cache of "Building Self-Attention and
-Transformer Engines" (codingpancake.com), section 6.2.
+Transformer Engines" (codingpancake.com), section 6.2, for decode and for a chunk appended into
+the blocks.
 """
 
 import math
@@ -15,7 +16,8 @@ import math
 import numpy as np
 import pytest
 
-from oracle import append_to_cache, attention, attention_with_cache, decode, decode_paged, rope, round_bf16
+from oracle import (append_to_cache, append_to_cache_paged, attention, attention_with_cache, decode, decode_paged,
+                    gather_pages, rope, round_bf16)
 from transformer_self_attention_amd import inputs
 
 
@@ -266,3 +268,49 @@ def test_paged_decode_brute_force_tiny():
         den = sum(w)
         want = [sum(w[t] / den * vp[bt[0, t // bs], kv, t % bs, d] for t in range(L)) for d in range(D)]
         assert np.allclose(o[0, h, 0], want, atol=1e-13)
+
+
+# --------------------------------------------------------------------------------------
+# A chunk appended into a paged cache
+# --------------------------------------------------------------------------------------
+@pytest.mark.parametrize("bs,pos0,Sq", [(4, 0, 9), (4, 6, 7), (8, 13, 3), (16, 5, 30)])
+def test_paged_append_equals_contiguous_append(bs, pos0, Sq):
+    """Writing the chunk into the blocks and reading the blocks back in table order gives the
+    contiguous cache after the contiguous append; pool slots of no sequence stay as they were."""
+    B, Hkv, D = 2, 3, 8
+    S = pos0 + Sq + 5
+    nb = -(-S // bs)
+    kc, vc = _rand((B, Hkv, S, D), 90), _rand((B, Hkv, S, D), 91)
+    kn, vn = _rand((B, Hkv, Sq, D), 92), _rand((B, Hkv, Sq, D), 93)
+    perm = np.random.default_rng(94).permutation(B * nb + 2)
+    kp, vp, bt = _pages_from_contiguous(kc, vc, bs, perm)
+    kp2, vp2 = append_to_cache_paged(kp, vp, bt, kn, vn, pos0)
+    kc2, vc2 = append_to_cache(kc, vc, kn, vn, pos0)
+    gk, gv = gather_pages(kp2, vp2, bt, S)
+    assert np.array_equal(gk, kc2) and np.array_equal(gv, vc2)
+    spare = perm[B * nb:]
+    assert np.array_equal(kp2[spare], kp[spare], equal_nan=True)
+    # only the chunk's slots changed
+    changed = np.argwhere(np.any(kp2 != kp, axis=(1, 3)) & ~np.isnan(kp).any(axis=(1, 3)))
+    want = {(int(bt[b, t // bs]), t % bs) for b in range(B) for t in range(pos0, pos0 + Sq)}
+    assert {(int(i), int(j)) for i, j in changed} <= want
+
+
+def test_paged_append_brute_force_tiny():
+    """Scalar loops: the rotated, bf16-rounded key of token t lands in its block's slot."""
+    Hkv, D, bs = 1, 4, 2
+    kp, vp = np.zeros((5, Hkv, bs, D)), np.zeros((5, Hkv, bs, D))
+    bt = np.array([[3, 0, 4]])
+    kn, vn = _rand((1, Hkv, 3, D), 95), _rand((1, Hkv, 3, D), 96)
+    kp2, vp2 = append_to_cache_paged(kp, vp, bt, kn, vn, 2)     # tokens 2, 3, 4
+    for i, t in enumerate((2, 3, 4)):
+        blk, slot = int(bt[0, t // bs]), t % bs
+        x = list(kn[0, 0, i])
+        for p in range(D // 2):
+            ang = t * 10000.0 ** (-(2.0 * p) / D)
+            c, s = math.cos(ang), math.sin(ang)
+            x[2 * p], x[2 * p + 1] = kn[0, 0, i, 2 * p] * c - kn[0, 0, i, 2 * p + 1] * s, \
+                kn[0, 0, i, 2 * p] * s + kn[0, 0, i, 2 * p + 1] * c
+        assert np.array_equal(kp2[blk, 0, slot], round_bf16(np.array(x)))
+        assert np.array_equal(vp2[blk, 0, slot], vn[0, 0, i])
+    assert np.all(kp2[3] == 0) and np.all(kp2[1] == 0)   # the blocks of tokens 0, 1 and no token: untouched
