@@ -210,6 +210,37 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
                                size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
+ * attn_prefill_chunk_paged: attn_prefill_chunk against a paged KV cache, the block pool of
+ * codingpancake.com "Building Self-Attention and Transformer Engines", section 6.2 (the cache
+ * attn_decode_paged reads).
+ *
+ * k_pages, v_pages: bf16 pools [num_blocks, Hkv, block_size, D]; block_table: device int32
+ * [B, max_blocks]; token t of sequence b is stored in block block_table[b * max_blocks +
+ * t / block_size], slot t % block_size.  block_size is a power of two in [16, 4096];
+ * pos0 + Sq <= max_blocks * block_size.
+ * Step 1 writes the slots of tokens pos0 .. pos0+Sq-1 (keys rotated at their positions and
+ *   rounded to bf16, values copied) and no other slot.  The blocks receiving them must not be
+ *   shared between sequences; blocks holding only earlier tokens may be.
+ * Step 2 is attn_prefill_chunk's: o[b, h, i] = softmax over tokens j <= pos0 + i (and, with a
+ *   window W >= 0, j >= pos0 + i - W) of sequence b.  Tokens before pos0 - W (the first query's
+ *   window start) are never read: blocks holding only such tokens, and their table entries,
+ *   may already have been released.
+ * workspace: required, at least attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D)
+ *   bytes, 16-byte aligned, contents irrelevant: it receives contiguous copies of the visible
+ *   key rows (IEEE half with RoPE, bf16 without) and value rows.
+ * Other arguments, the support matrix and the errors as in attn_prefill_chunk; also
+ * ATTN_ERR_INVALID_ARG for a bad block size, a null or misaligned block table, or a chunk
+ * past the table.  Table entries outside [0, num_blocks) are clamped into it.
+ * --------------------------------------------------------------------------------------- */
+size_t attn_prefill_chunk_paged_workspace_bytes(int B, int Hkv, int pos0, int Sq, int D);
+attn_status attn_prefill_chunk_paged(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                     void* v_pages, int num_blocks, int block_size,
+                                     const int32_t* block_table, int max_blocks, void* o, float* lse,
+                                     attn_dtype out_dt, int B, int Hq, int Hkv, int Sq, int D, int pos0,
+                                     int window, const float* rope_table, int table_max_pos,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV
  * cache and the memory wall"), split over the cache length ("split-K") with a merge pass.
  *

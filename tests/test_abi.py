@@ -209,6 +209,41 @@ def test_prefill_chunk_rejects(kw, code):
     assert _chunk(**kw) == code
 
 
+def _chunk_paged(**kw):
+    a = dict(q=A, kn=A, vn=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=20, o=A, lse=None, out_dt=BF16, B=2, Hq=8,
+             Hkv=2, Sq=100, D=128, pos0=50, window=-1, table=A, tmax=300, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = 2 * 2 * 2 * (50 + 100) * 128 * 2
+    return lib.raw().attn_prefill_chunk_paged(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["nblk"], a["bs"],
+                                              a["bt"], a["mb"], a["o"], a["lse"], a["out_dt"], a["B"], a["Hq"],
+                                              a["Hkv"], a["Sq"], a["D"], a["pos0"], a["window"], a["table"],
+                                              a["tmax"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_chunk_paged_workspace_bytes():
+    assert lib.prefill_chunk_paged_workspace_bytes(1, 8, 6144, 2048, 128) == 2 * 8 * 8192 * 128 * 2
+    assert lib.prefill_chunk_paged_workspace_bytes(0, 8, 0, 10, 128) == 0
+    assert lib.prefill_chunk_paged_workspace_bytes(1, 8, -1, 10, 128) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kn=None), INV), (dict(vn=None), INV), (dict(kp=None), INV), (dict(vp=None), INV),
+    (dict(bt=None), INV), (dict(o=None), INV), (dict(ws=None), INV), (dict(table=None, ws=None), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(D=0), INV),
+    (dict(pos0=-1), INV), (dict(Hq=8, Hkv=3), INV), (dict(nblk=0), INV), (dict(mb=0), INV),
+    (dict(bs=8), INV), (dict(bs=24), INV), (dict(bs=8192), INV),
+    (dict(mb=9), INV),                                       # pos0 + Sq > max_blocks * block_size
+    (dict(tmax=149), INV),                                   # table too short for the last position
+    (dict(wsb=2 * 2 * 2 * 150 * 128 * 2 - 1), INV), (dict(ws=MIS), INV),
+    (dict(q=MIS), INV), (dict(kp=MIS), INV), (dict(vn=MIS), INV), (dict(lse=MIS), INV),
+    (dict(bt=P(0x10002)), INV), (dict(table=MIS), INV), (dict(D=65), INV), (dict(out_dt=5), INV),
+    (dict(D=96, wsb=1 << 30), UNSUP), (dict(D=256, wsb=1 << 30), UNSUP),
+])
+def test_prefill_chunk_paged_rejects(kw, code):
+    assert _chunk_paged(**kw) == code
+
+
 def _paged(**kw):
     a = dict(q=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=64, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16,
              B=4, Hq=16, Hkv=2, D=128, window=-1, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)

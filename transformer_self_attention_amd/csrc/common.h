@@ -104,6 +104,14 @@ hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hi
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
                                int conv_first, const float* table, hipStream_t st);
+// The same for a paged cache: pools [num_blocks, Hkv, 1 << bs_log2, D] and a block table
+// [B, max_blocks].  The new rows go into their blocks; rows [conv_first, pos0 + Sq) are also
+// gathered into k_ws (fp16 with RoPE, bf16 without) and v_ws (bf16), both [B*Hkv, pos0 + Sq, D]
+// (rows before first_seen, which no query sees, as zeros without reading them).
+hipError_t launch_cache_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                     const int32_t* block_table, int max_blocks, int bs_log2, int num_blocks,
+                                     void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D, int pos0,
+                                     int conv_first, int first_seen, const float* table, hipStream_t st);
 // The attention of a chunk against the cache: a.k holds the fp16 keys (a.table != nullptr) or
 // the bf16 cache keys (no RoPE).
 hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st);

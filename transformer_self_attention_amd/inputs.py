@@ -306,3 +306,41 @@ def make_paged_decode(wl: Workload, *, block_size: int = 16, spare_blocks: int =
 
     return PagedDecodeInputs(wl, d.q, scatter(d.k_cache.bits), scatter(d.v_cache.bits), table, d.cache_len,
                              d.q_pos, block_size, d)
+
+
+@dataclasses.dataclass
+class PagedChunkInputs:
+    wl: Workload
+    chunk: ChunkInputs        # the same draws with the cache contiguous
+    k_pages: Tensor           # [num_blocks, Hkv, block_size, D]: the cache cut into blocks
+    v_pages: Tensor
+    block_table: np.ndarray   # int32 [B, max_blocks]
+    block_size: int
+
+
+def make_paged_chunk(wl: Workload, *, block_size: int = 16, spare_blocks: int = 5,
+                     seed: Optional[int] = None) -> PagedChunkInputs:
+    """The inputs of make_chunk (same draws), with the cache [B, Hkv, S_max, D] cut into blocks of
+    block_size tokens scattered over a pool in a seeded random order.  Pool slots of no
+    sequence (spare blocks, the tail of each sequence's last block) hold bf16 NaN.  The layout
+    draws come from their own stream (seed + 1000003), after nothing else."""
+    c = make_chunk(wl, seed=seed)
+    seed = wl.seed if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed + 1000003))
+    B, Hkv, S, D = wl.B, wl.Hkv, wl.S_max, wl.D
+    nb = -(-S // block_size)
+    num_blocks = B * nb + spare_blocks
+    perm = rng.permutation(num_blocks)
+    table = perm[:B * nb].reshape(B, nb).astype(np.int32)
+
+    def scatter(bits):
+        pool = np.full((num_blocks, Hkv, block_size, D), BF16_NAN_BITS, dtype=np.uint16)
+        padded = np.full((B, Hkv, nb * block_size, D), BF16_NAN_BITS, dtype=np.uint16)
+        padded[:, :, :S] = bits
+        blocks = padded.reshape(B, Hkv, nb, block_size, D).transpose(0, 2, 1, 3, 4).reshape(B * nb, Hkv,
+                                                                                            block_size, D)
+        pool[perm[:B * nb]] = blocks
+        return Tensor.from_bf16_bits(pool)
+
+    return PagedChunkInputs(wl, c, scatter(c.k_cache.bits), scatter(c.v_cache.bits), table, block_size)
+

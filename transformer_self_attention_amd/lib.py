@@ -31,6 +31,8 @@ EXPORTED = (
     "attn_rotate_keys_f16",
     "attn_prefill_prerotated",
     "attn_prefill_chunk",
+    "attn_prefill_chunk_paged_workspace_bytes",
+    "attn_prefill_chunk_paged",
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
@@ -76,6 +78,11 @@ def _load():
     lib.attn_prefill_chunk.restype = i32
     lib.attn_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
                                        i32, fp, i32, vp, sz, vp]
+    lib.attn_prefill_chunk_paged_workspace_bytes.restype = sz
+    lib.attn_prefill_chunk_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    lib.attn_prefill_chunk_paged.restype = i32
+    lib.attn_prefill_chunk_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, fp, i32, i32, i32, i32,
+                                             i32, i32, i32, i32, fp, i32, vp, sz, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
@@ -317,6 +324,54 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, window
     _check(_lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                    _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _win(window), _ptr(table),
                                    tmax, _ptr(workspace), wsb, _stream(stream)), "attn_prefill_chunk")
+    return out
+
+
+def prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D) -> int:
+    return int(_lib.attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D))
+
+
+def prefill_chunk_paged(q, k_new, v_new, k_pages, v_pages, block_table, pos0, table=None, *, window=None,
+                        out=None, out_dtype=None, lse=None, workspace=None, stream=None):
+    """prefill_chunk() against a paged cache: pools [num_blocks, Hkv, block_size, D] and an int32
+    block table [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size]).
+    The chunk's keys and values go into their blocks; workspace: uint8 GPU tensor of
+    >= prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D) bytes, allocated here when None."""
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    _need(block_table, "block_table")
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be int32 [B, max_blocks]")
+    B, Hq, Sq, D = q.shape
+    num_blocks, Hkv, bs = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    if k_new.shape != (B, Hkv, Sq, D) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B, Hkv, Sq, D]")
+    if k_pages.shape != (num_blocks, Hkv, bs, D) or v_pages.shape != k_pages.shape:
+        raise ValueError("k_pages and v_pages must be [num_blocks, Hkv, block_size, D]")
+    if block_table.shape[0] != B:
+        raise ValueError("block_table must have one row per sequence")
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
+    _need(out, "out")
+    if lse is not None:
+        _need(lse, "lse")
+        if lse.dtype != torch.float32 or lse.numel() != B * Hq * Sq:
+            raise ValueError("lse must be float32 [B, Hq, Sq]")
+    tmax = 0
+    if table is not None:
+        _need(table, "table")
+        tmax = table.shape[0]
+    if workspace is None:
+        workspace = torch.empty(max(prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D), 16),
+                                dtype=torch.uint8, device=q.device)
+    _need(workspace, "workspace")
+    _check(_lib.attn_prefill_chunk_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                         num_blocks, bs, _ptr(block_table), block_table.shape[1], _ptr(out),
+                                         _ptr(lse), _dt(out), B, Hq, Hkv, Sq, D, pos0, _win(window), _ptr(table),
+                                         tmax, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                         _stream(stream)), "attn_prefill_chunk_paged")
     return out
 
 
