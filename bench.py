@@ -23,7 +23,9 @@ One step = one pass of the hot path over the workload's synthetic batch:
   * chunk (sub-object ``chunk_prefill``): the last 2048-token chunk of an 8192-token GQA prompt
     (B=1, Hq=64, Hkv=8, D=128) against the 6144 tokens already in the KV cache; one
     attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
-    chunk's queries against cache rows [0, 8192) with the bottom-right causal mask).
+    chunk's queries against cache rows [0, 8192) with the bottom-right causal mask); and
+    (``paged_chunk_prefill``) the same chunk against the cache in 16-token blocks scattered over
+    a pool, one attn_prefill_chunk_paged call.
 
 Inputs are resident in HBM before timing starts.  W untimed warmup steps, then K timed steps
 bracketed by torch.cuda.synchronize(), timed with HIP events recorded on the stream the library
@@ -254,7 +256,19 @@ def bench_chunk(lib, inputs, wl, steps, warmup):
                     steps, warmup)
     tf = wl.chunk_flops() / (ms * 1e-3) / 1e12
     log(f"[bench] chunk prefill: {ms:.4f} ms/step, {tf:.1f} TFLOP/s")
-    return {"c": c, "ms": ms, "tflops": tf}
+    # the same chunk against the cache cut into 16-token blocks scattered over a pool
+    pc = inputs.make_paged_chunk(wl, block_size=16)
+    kp, vp = pc.k_pages.torch("cuda"), pc.v_pages.torch("cuda")
+    bt = torch.from_numpy(pc.block_table).cuda()
+    wsp = torch.empty(lib.prefill_chunk_paged_workspace_bytes(wl.B, wl.Hkv, wl.pos0, wl.S, wl.D),
+                      dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] timing paged chunk prefill: warmup {warmup}, steps {steps}")
+    ms_p = time_calls(lambda: lib.prefill_chunk_paged(q, kn, vn, kp, vp, bt, wl.pos0, tab, out=out, workspace=wsp),
+                      steps, warmup)
+    tf_p = wl.chunk_flops() / (ms_p * 1e-3) / 1e12
+    log(f"[bench] paged chunk prefill: {ms_p:.4f} ms/step, {tf_p:.1f} TFLOP/s")
+    return {"c": c, "ms": ms, "tflops": tf, "ms_paged": ms_p, "tflops_paged": tf_p}
 
 
 def cpu_threads():
@@ -471,6 +485,12 @@ def main():
             "frac": round(r["tflops"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "config": {"workload": "chunked prefill against a KV cache (append, then attend)", "B": wl.B,
                        "Hq": wl.Hq, "Hkv": wl.Hkv, "chunk_len": wl.S, "pos0": wl.pos0, "S_max": wl.S_max,
+                       "head_dim": wl.D, "flops_per_step": wl.chunk_flops()}}
+        out["paged_chunk_prefill"] = {
+            "value": round(r["tflops_paged"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_paged"], 5),
+            "frac": round(r["tflops_paged"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "config": {"workload": "chunked prefill into a paged KV cache (16-token blocks, shuffled)", "B": wl.B,
+                       "Hq": wl.Hq, "Hkv": wl.Hkv, "chunk_len": wl.S, "pos0": wl.pos0, "block_size": 16,
                        "head_dim": wl.D, "flops_per_step": wl.chunk_flops()}}
     if not args.no_cpu_baseline:
         if "prefill" in res:
