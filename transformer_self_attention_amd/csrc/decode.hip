@@ -8,10 +8,12 @@
 // (codingpancake.com section 6.1) are processed together so each K/V byte is read once.
 //
 // decode_split_kernel, one workgroup per (sequence, KV head, group of up to 16 query heads, split):
-//  * The G query heads of a KV head fill the 16 columns of the MFMA B operand; with G > 16 (as in
-//    multi-query attention, one KV head for every query head) they are taken 16 at a time by
-//    separate workgroups.  Those workgroups get consecutive slots on the same XCD (workgroup ids
-//    are dealt to the 8 XCDs in turn), so their reads of the same K/V meet in that XCD's L2.
+//  * The G query heads of a KV head fill the 16 columns of the MFMA B operand.  More than 16
+//    (multi-query attention) go to decode_wide_kernel (decode_wide.hip), which shares each K/V
+//    tile among up to 64 of them; only a cache or pool over 2 GiB, beyond that kernel's 32-bit
+//    offsets, comes here with G > 16: the query heads are then taken 16 at a time by separate
+//    workgroups on consecutive slots of one XCD (workgroup ids are dealt to the 8 XCDs in turn),
+//    so their reads of the same K/V meet in that XCD's L2.
 //  * The waves stream disjoint 32-key sub-blocks of the split; loads of sub-block i+1 are in
 //    flight while sub-block i is consumed (16 x 16-byte loads per lane).  The cache is read once,
 //    so its loads are nontemporal (streaming) and do not displace reusable lines in the caches.
