@@ -61,11 +61,11 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 160448.3 KiB, WRITE_SIZE 131072.0 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 462815796, "sources_sha256_16": "b9bf9bcb45ff1686"},
+    # FETCH_SIZE 160503.4 KiB, WRITE_SIZE 131072.0 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 462928624, "sources_sha256_16": "b1c6635824e32d9c"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
-    # FETCH_SIZE 528546.1 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1082986744, "sources_sha256_16": "5f038f12710d4d5e"},
+    # FETCH_SIZE 528564.7 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1083024752, "sources_sha256_16": "c953fb4373c29e42"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
