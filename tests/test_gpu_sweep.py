@@ -1,9 +1,9 @@
 """Seeded sweeps over shapes and options of every attention entry point, against the fp64 oracle.
 
-Each case draws its configuration from a seeded generator (batch, heads and group size, lengths
-that are not tile multiples, head dim, window, position offset, output dtype, key mode, split
-count, block size) and checks the HIP result with the bf16 bars.  The configuration is printed
-before each launch.
+Each case draws its configuration from a seeded generator (batch, heads and group size up to 64
+query heads per KV head, lengths that are not tile multiples, head dim, window, position offset,
+output dtype, key mode, split count, block size) and checks the HIP result with the bf16 bars.
+The configuration is printed before each launch.
 """
 
 import numpy as np
@@ -26,7 +26,7 @@ def lib():
 
 def _heads(rng):
     Hkv = int(rng.choice([1, 2, 4]))
-    G = int(rng.choice([1, 2, 3, 4, 8, 16, 20, 32]))
+    G = int(rng.choice([1, 2, 3, 4, 8, 16, 20, 32, 48, 64]))
     return Hkv * G, Hkv
 
 
@@ -121,4 +121,35 @@ def test_chunk_sweep(lib, seed):
     ref_k, ref_v = oracle.append_to_cache(c.k_cache.f64(), c.v_cache.f64(), c.k_new.f64(), c.v_new.f64(), pos0,
                                           rope_base=base)
     ref, _ = oracle.attention_with_cache(c.q.f64(), ref_k, ref_v, pos0, rope_base=base, window=W)
+    assert_bf16_parity(to_np(o), ref, "o")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_paged_chunk_sweep(lib, seed):
+    rng = np.random.default_rng(7000 + seed)
+    Hq, Hkv = _heads(rng)
+    B = int(rng.integers(1, 3))
+    Sq = int(rng.integers(1, 300))
+    pos0 = int(rng.integers(0, 700))
+    S_max = pos0 + Sq + int(rng.integers(0, 50))
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64, 256]))
+    W = int(rng.integers(0, pos0 + Sq + 10)) if rng.random() < 0.4 else None
+    rope = bool(rng.random() < 0.8)
+    banner(f"paged chunk sweep seed={seed}: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} pos0={pos0} S_max={S_max} D={D} "
+           f"bs={bs} W={W} rope={rope}")
+    wl = inputs.Workload("c", B=B, Hq=Hq, Hkv=Hkv, S=Sq, D=D, dtype="bf16", seed=8000 + seed, kind="chunk",
+                         pos0=pos0, S_max=S_max)
+    p = inputs.make_paged_chunk(wl, block_size=bs)
+    c = p.chunk
+    tab = lib.make_rope_table(S_max, D) if rope else None
+    o = lib.prefill_chunk_paged(c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda"),
+                                p.k_pages.torch("cuda"), p.v_pages.torch("cuda"), torch.from_numpy(p.block_table).cuda(),
+                                pos0, tab, window=W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    base = 10000.0 if rope else None
+    rk, rv = oracle.append_to_cache_paged(p.k_pages.f64(), p.v_pages.f64(), p.block_table, c.k_new.f64(),
+                                          c.v_new.f64(), pos0, rope_base=base)
+    ck, cv = oracle.gather_pages(rk, rv, p.block_table, pos0 + Sq)
+    ref, _ = oracle.attention_with_cache(c.q.f64(), ck, cv, pos0, rope_base=base, window=W)
     assert_bf16_parity(to_np(o), ref, "o")
