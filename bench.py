@@ -217,6 +217,35 @@ def reference_gemm_tflops(n=8192, iters=20):
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def reference_sdpa_tflops(wl, iters=10):
+    """torch's own fused causal attention (scaled_dot_product_attention, flash backend only) on a
+    prefill of the same shape, timed like the prefill: context for the library's prefill rate.
+    K and V heads are repeated to Hq (the backend takes equal head counts) and no rotation is
+    applied, so it does less work than the library's step.  None where the backend is missing."""
+    import torch
+    try:
+        from torch.nn.attention import sdpa_kernel, SDPBackend
+    except ImportError:
+        return None
+    g = torch.Generator(device="cuda").manual_seed(wl.seed)
+    q = torch.randn(wl.B, wl.Hq, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
+    k = torch.randn(wl.B, wl.Hkv, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
+    v = torch.randn(wl.B, wl.Hkv, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
+    if wl.Hkv != wl.Hq:
+        k = k.repeat_interleave(wl.Hq // wl.Hkv, dim=1).contiguous()
+        v = v.repeat_interleave(wl.Hq // wl.Hkv, dim=1).contiguous()
+    sdpa = torch.nn.functional.scaled_dot_product_attention
+    try:
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            ms = time_calls(lambda: sdpa(q, k, v, is_causal=True), iters, 3)
+    except RuntimeError as ex:
+        log(f"[bench] torch SDPA flash backend unavailable: {str(ex)[:120]}")
+        return None
+    finally:
+        del q, k, v
+    return wl.prefill_flops() / (ms * 1e-3) / 1e12
+
+
 def bench_paged_decode(lib, inputs, wl, steps, warmup, block_size=16):
     import torch
     log(f"[bench] generating paged decode inputs B={wl.B} cache={wl.S} block={block_size}")
@@ -354,6 +383,10 @@ def main():
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
         res["gemm_tflops"] = reference_gemm_tflops()
         log(f"[bench] reference: torch bf16 GEMM 8192^3 {res['gemm_tflops']:.1f} TFLOP/s")
+        res["sdpa_tflops"] = reference_sdpa_tflops(W["gqa"])
+        if res["sdpa_tflops"] is not None:
+            log(f"[bench] reference: torch SDPA flash, same shape, K/V heads repeated, no RoPE "
+                f"{res['sdpa_tflops']:.1f} TFLOP/s")
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("mha", "all"):
@@ -395,8 +428,12 @@ def main():
                        "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D, "causal": True,
                        "rope_base": wl.rope_base, "flops_per_step": wl.prefill_flops()},
             "context": {"torch_bf16_gemm_8192_tflops": round(res["gemm_tflops"], 1),
+                        "torch_sdpa_flash_causal_tflops": (None if res["sdpa_tflops"] is None
+                                                           else round(res["sdpa_tflops"], 1)),
                         "note": "the vendor GEMM on the same GPU in the same run: what plain bf16 matrix "
-                                "work reaches under this part's power limit"},
+                                "work reaches under this part's power limit; torch's flash SDPA backend "
+                                "on the same shape with K/V heads repeated to Hq and no RoPE (less "
+                                "work than this step), timed the same way"},
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated fp16 keys)",
                          "achieved": round(kt, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(kt / MFMA_BF16_PEAK_TFLOPS, 4),
