@@ -207,6 +207,24 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
 
 
+def bench_rope(lib, p, steps, warmup):
+    """attn_rope_apply on the prefill's Q ([B, Hq, S, D] bf16), out of place and in place.  It
+    reads and writes the tensor once: 2 x its bytes per call (the coefficient table, 8 bytes per
+    pair and position, is reused across heads from L2)."""
+    import torch
+    wl = p.wl
+    x = p.q.torch("cuda")
+    tab = lib.make_rope_table(wl.S, wl.D)
+    out = torch.empty_like(x)
+    nbytes = 2 * x.numel() * x.element_size()
+    ms = time_calls(lambda: lib.rope_apply(x, tab, 0, out), steps, warmup)
+    ms_in = time_calls(lambda: lib.rope_apply(out, tab, 0, out), steps, warmup)
+    log(f"[bench] rope_apply {list(x.shape)} bf16: {ms * 1e3:.1f} us ({nbytes / ms / 1e6:.1f} GB/s), "
+        f"in place {ms_in * 1e3:.1f} us")
+    del x, out
+    return {"ms": ms, "ms_in_place": ms_in, "bytes": nbytes, "shape": list(p.q.shape)}
+
+
 def reference_gemm_tflops(n=8192, iters=20):
     """torch.matmul bf16 n x n x n on the same GPU, timed like the prefill: what the vendor GEMM
     reaches under this part's power limit (context for the prefill's fraction of peak)."""
@@ -381,6 +399,7 @@ def main():
         del src, dst
     if args.only in ("prefill", "all"):
         res["prefill"] = bench_prefill(lib, inputs, W["gqa"], args.steps, args.warmup)
+        res["rope"] = bench_rope(lib, res["prefill"]["p"], 4 * args.steps, 4 * args.warmup)
         res["gemm_tflops"] = reference_gemm_tflops()
         log(f"[bench] reference: torch bf16 GEMM 8192^3 {res['gemm_tflops']:.1f} TFLOP/s")
         res["sdpa_tflops"] = reference_sdpa_tflops(W["gqa"])
@@ -441,6 +460,14 @@ def main():
                          "flops_per_launch": wl.prefill_flops(),
                          "algorithmic_bytes_per_launch": wl.prefill_bytes()},
         })
+    if "rope" in res:
+        r = res["rope"]
+        gbs = r["bytes"] / (r["ms"] * 1e-3) / 1e9
+        out["rope_apply"] = {
+            "value": round(gbs, 1), "unit": "GB/s", "ms_per_call": round(r["ms"], 5),
+            "ms_per_call_in_place": round(r["ms_in_place"], 5), "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "config": {"workload": "RoPE on the GQA prefill's Q, out of place", "shape": r["shape"],
+                       "dtype": "bf16", "bytes_per_call": r["bytes"]}}
     if "decode" in res:
         r = res["decode"]
         wl = r["d"].wl
