@@ -63,13 +63,19 @@ def test_rope_apply_dim8_example(lib):
     assert abs(np.linalg.norm(got[0, 0, 5]) - np.linalg.norm(g["token_vec_b"])) < 1e-6
 
 
-@pytest.mark.parametrize("dtype,D,S,pos0,inplace", [("bf16", 128, 37, 0, False), ("bf16", 64, 200, 5, True),
-                                                    ("f32", 128, 129, 3, False), ("f32", 6, 11, 0, True),
-                                                    ("bf16", 10, 7, 2, False)])
-def test_rope_apply_random(lib, dtype, D, S, pos0, inplace):
-    banner(f"rope_apply {dtype} D={D} S={S} pos0={pos0} inplace={inplace}")
+# B x H row blocks: 6 (a full group of 4 heads per lane plus 2), 12 (whole groups), 1, 13
+@pytest.mark.parametrize("dtype,D,S,pos0,inplace,BH", [("bf16", 128, 37, 0, False, (2, 3)),
+                                                       ("bf16", 64, 200, 5, True, (2, 3)),
+                                                       ("f32", 128, 129, 3, False, (2, 3)),
+                                                       ("f32", 6, 11, 0, True, (2, 3)),
+                                                       ("bf16", 10, 7, 2, False, (2, 3)),
+                                                       ("bf16", 128, 65, 1, True, (3, 4)),
+                                                       ("f32", 64, 50, 0, False, (1, 1)),
+                                                       ("bf16", 128, 33, 4, False, (1, 13))])
+def test_rope_apply_random(lib, dtype, D, S, pos0, inplace, BH):
+    banner(f"rope_apply {dtype} B,H={BH} D={D} S={S} pos0={pos0} inplace={inplace}")
     rng = np.random.default_rng(D * 1000 + S)
-    x = inputs.Tensor(rng.standard_normal((2, 3, S, D)).astype(np.float32), dtype)
+    x = inputs.Tensor(rng.standard_normal((*BH, S, D)).astype(np.float32), dtype)
     tab = lib.make_rope_table(pos0 + S, D)
     xt = dev(x)
     out = lib.rope_apply(xt, tab, pos0=pos0, out=xt if inplace else None)
