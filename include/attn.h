@@ -29,6 +29,9 @@
  *     calls, never synchronises, and enqueues its kernels on `stream` (a hipStream_t;
  *     NULL means the default stream).  Calls are asynchronous: a returned ATTN_OK means
  *     the work was enqueued.
+ *   - Only kernel launches reach the stream (no memset, copy or event), so a call made
+ *     while the stream is being captured into a HIP graph is captured whole and can be
+ *     replayed; its buffers must then stay allocated for as long as the graph is used.
  *   - Every argument that can be checked on the host is checked before any HIP call; a
  *     rejected call enqueues nothing.  HIP launch errors map to ATTN_ERR_HIP.
  *   - No C++ exception crosses this interface.  Calls are thread-safe (no shared state).
