@@ -60,9 +60,9 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # Calibration (1 GiB device-to-device copy, __amd_rocclr_copyBuffer): FETCH_SIZE reads 524302 KiB
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
-    # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (8 dispatches):
-    # FETCH_SIZE 160503.4 KiB, WRITE_SIZE 131072.0 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 462928624, "sources_sha256_16": "b1c6635824e32d9c"},
+    # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (11 dispatches):
+    # FETCH_SIZE 160599.4 KiB, WRITE_SIZE 131072.0 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 463125245, "sources_sha256_16": "218bfa802c0363cc"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
     # FETCH_SIZE 528564.7 KiB, WRITE_SIZE 512.0 KiB per step.
     "decode": {"bytes_per_launch": 1083024752, "sources_sha256_16": "c953fb4373c29e42"},

@@ -318,9 +318,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       bf16x8 pf[2][2];
       float lsum = 0.f;
       // p = 2^score rounded to bf16 (the B operand of P.V); the row sum adds the same rounded
-      // weights, two at a time (v_dot2_f32_bf16 against (1, 1))
+      // weights, two at a time (v_dot2_f32_bf16 against (1, 1)), in two independent chains
       auto weights = [&]() __attribute__((always_inline)) {
-        lsum = 0.f;
+        float ls[2] = {0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -332,8 +332,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
               pp[1] = (__bf16)fast_exp2(sacc[kb][8 * s + tt + 1]);
               pf[kb][s][tt] = pp[0];
               pf[kb][s][tt + 1] = pp[1];
-              lsum = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, lsum, false);
+              ls[kb] = __builtin_amdgcn_fdot2_f32_bf16(pp, ones, ls[kb], false);
             }
+        lsum = ls[0] + ls[1];
       };
       auto tile_max = [&]() __attribute__((always_inline)) {
         float mx = sacc[0][0];
