@@ -130,13 +130,14 @@ def time_calls(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps
 
 
-def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
+def bench_prefill(lib, inputs, wl, steps, warmup, variants=True, out_dtype=None):
+    """out_dtype: the output's dtype (None: the inputs' bf16)."""
     import torch
     log(f"[bench] generating {wl.name} prefill inputs B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} S={wl.S} D={wl.D}")
     p = inputs.make_prefill(wl)
     q, k, v = p.q.torch("cuda"), p.k.torch("cuda"), p.v.torch("cuda")
     tab = lib.make_rope_table(wl.S, wl.D)
-    out = torch.empty_like(q)
+    out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     ws = torch.empty(lib.prefill_workspace_bytes(wl.B, wl.Hkv, wl.S, wl.D), dtype=torch.uint8, device="cuda")
     krot = ws.view(torch.float16).view(k.shape)
     torch.cuda.synchronize()
@@ -172,7 +173,7 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True):
         lib.prefill_prerotated(q, krot, v, tab, window=W, out=out)
         c.record(stream)
     torch.cuda.synchronize()
-    r = {"p": p, "ms_step": ms_step,
+    r = {"p": p, "ms_step": ms_step, "out_dtype": str(out.dtype).replace("torch.", ""),
          "kernel_ms": _stats([b.elapsed_time(c) for _, b, c in marks]),
          "rotate_ms": _stats([a.elapsed_time(b) for a, b, _ in marks])}
     r["tflops_step"] = flops / (r["ms_step"] * 1e-3) / 1e12
@@ -240,35 +241,6 @@ def reference_gemm_tflops(n=8192, iters=20):
     b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
     ms = time_calls(lambda: a @ b, iters, 5)
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
-
-
-def reference_sdpa_tflops(wl, iters=10):
-    """torch's own fused causal attention (scaled_dot_product_attention, flash backend only) on a
-    prefill of the same shape, timed like the prefill: context for the library's prefill rate.
-    K and V heads are repeated to Hq (the backend takes equal head counts) and no rotation is
-    applied, so it does less work than the library's step.  None where the backend is missing."""
-    import torch
-    try:
-        from torch.nn.attention import sdpa_kernel, SDPBackend
-    except ImportError:
-        return None
-    g = torch.Generator(device="cuda").manual_seed(wl.seed)
-    q = torch.randn(wl.B, wl.Hq, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
-    k = torch.randn(wl.B, wl.Hkv, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
-    v = torch.randn(wl.B, wl.Hkv, wl.S, wl.D, device="cuda", dtype=torch.bfloat16, generator=g)
-    if wl.Hkv != wl.Hq:
-        k = k.repeat_interleave(wl.Hq // wl.Hkv, dim=1).contiguous()
-        v = v.repeat_interleave(wl.Hq // wl.Hkv, dim=1).contiguous()
-    sdpa = torch.nn.functional.scaled_dot_product_attention
-    try:
-        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
-            ms = time_calls(lambda: sdpa(q, k, v, is_causal=True), iters, 3)
-    except Exception as ex:  # context only: a missing or failing backend must not end the bench
-        log(f"[bench] torch SDPA flash backend unavailable: {type(ex).__name__}: {str(ex)[:120]}")
-        return None
-    finally:
-        del q, k, v
-    return wl.prefill_flops() / (ms * 1e-3) / 1e12
 
 
 def bench_paged_decode(lib, inputs, wl, steps, warmup, block_size=16):
@@ -409,10 +381,6 @@ def main():
         res["rope"] = bench_rope(lib, res["prefill"]["p"], 4 * args.steps, 4 * args.warmup)
         res["gemm_tflops"] = reference_gemm_tflops()
         log(f"[bench] reference: torch bf16 GEMM 8192^3 {res['gemm_tflops']:.1f} TFLOP/s")
-        res["sdpa_tflops"] = reference_sdpa_tflops(W["gqa"])
-        if res["sdpa_tflops"] is not None:
-            log(f"[bench] reference: torch SDPA flash, same shape, K/V heads repeated, no RoPE "
-                f"{res['sdpa_tflops']:.1f} TFLOP/s")
     if args.only in ("decode", "all"):
         res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
     if args.only in ("mha", "all"):
@@ -428,8 +396,11 @@ def main():
     if args.only in ("chunk", "all"):
         res["chunk"] = bench_chunk(lib, inputs, W["chunk"], args.steps, args.warmup)
     if args.only == "long" or (args.only == "all" and not args.no_long):
+        # float32 output: rounding the exact result of this workload to bf16 alone costs a mean
+        # abs error of 8.6e-4 (rows dominated by one scaled key have |o| ~ |v|), so only the fp32
+        # output is within both parity bars against the exact result: that is the output timed
         res["long"] = bench_prefill(lib, inputs, W["long"], max(3, args.steps // 5), max(2, args.warmup // 5),
-                                    variants=False)
+                                    variants=False, out_dtype=torch.float32)
 
     out = {
         "metric": "causal GQA prefill TFLOP/s (% MFMA peak); decode KV-read GB/s (% HBM peak)",
@@ -454,12 +425,8 @@ def main():
                        "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D, "causal": True,
                        "rope_base": wl.rope_base, "flops_per_step": wl.prefill_flops()},
             "context": {"torch_bf16_gemm_8192_tflops": round(res["gemm_tflops"], 1),
-                        "torch_sdpa_flash_causal_tflops": (None if res["sdpa_tflops"] is None
-                                                           else round(res["sdpa_tflops"], 1)),
-                        "note": "the vendor GEMM on the same GPU in the same run: what plain bf16 matrix "
-                                "work reaches under this part's power limit; torch's flash SDPA backend "
-                                "on the same shape with K/V heads repeated to Hq and no RoPE (less "
-                                "work than this step), timed the same way"},
+                        "note": "a plain bf16 matrix product (8192^3) on the same GPU in the same run: "
+                                "what dense matrix work alone reaches under this part's power limit"},
             "roofline": {"bound": "mfma", "kernel": "prefill_bf16_kernel (pre-rotated fp16 keys)",
                          "achieved": round(kt, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(kt / MFMA_BF16_PEAK_TFLOPS, 4),
@@ -509,8 +476,10 @@ def main():
             "frac": round(r["tflops_step"] / MFMA_BF16_PEAK_TFLOPS, 4),
             "attention_kernel_tflops": round(r["tflops_kernel"], 2),
             "attention_kernel_frac": round(r["tflops_kernel"] / MFMA_BF16_PEAK_TFLOPS, 4),
-            "config": {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
-                       "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale}}
+            "config": {"workload": "long-context causal GQA prefill with RoPE, 1% of keys scaled by 8",
+                       "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "seq_len": wl.S, "head_dim": wl.D,
+                       "big_key_frac": wl.big_key_frac, "big_key_scale": wl.big_key_scale,
+                       "input_dtype": "bf16", "output_dtype": r["out_dtype"]}}
     if "swa" in res:
         r = res["swa"]
         wl = r["p"].wl

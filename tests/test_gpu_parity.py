@@ -184,26 +184,30 @@ def test_prefill_gqa_config(lib):
 def test_prefill_long_config(lib):
     """Long workload at full size: S=32768, 1% of keys x8; 128 seeded rows per head.
 
-    Checked with fp32 output against both bars.  Rounding the exact result to bf16 storage alone
-    costs a mean abs error of ~8.6e-4 on this workload (the rows dominated by a x8 key have |o|
-    near |v|), so the bf16-output run is held to the max-abs bar against the exact result and to
-    the mean-abs bar against the exact result rounded once to bf16 (same storage precision)."""
+    The fp32 output (the output the benchmark times for this workload) is held to both bars
+    against the exact fp64 result, with either key path.  A bf16 output cannot be: rounding the
+    exact result to bf16 alone costs a mean abs error of ~8.6e-4 here (the rows dominated by a
+    x8 key have |o| near |v|), and with the kernel's own error the bf16 output measures ~1.01e-3.
+    The bf16 output is therefore checked to be exactly the fp32 result rounded to bf16 (the
+    kernels differ only in the final store), and held to the max-abs bar against the exact
+    result; its mean against the exact result is printed, not asserted."""
     wl = inputs.WORKLOADS["long"]
     banner("prefill long Hq=32 Hkv=8 S=32768 x8 keys (full config, 128 rows/head)")
     p = inputs.make_prefill(wl)
     ref, ref_lse = oracle_rows(p, rows=p.rows)
+    o32 = None
     for ws in (True, False):
         o, lse = run_prefill(lib, p, out_dtype=torch.float32, workspace=ws)
         assert_bf16_parity(take_rows(to_np(o), p.rows), ref, f"long o (fp32 out, workspace={ws})")
         assert err_stats(take_rows(to_np(lse), p.rows), ref_lse)[0] < 2e-2
-    ob, _ = run_prefill(lib, p, out_dtype=torch.bfloat16)
+        if ws:
+            o32 = o
+    ob, _ = run_prefill(lib, p, out_dtype=torch.bfloat16, workspace=True)
+    assert torch.equal(ob, o32.to(torch.bfloat16)), "bf16 output is not the fp32 result rounded to bf16"
     mx, mean = err_stats(take_rows(to_np(ob), p.rows), ref)
-    print(f"    long o (bf16 out) max_abs={mx:.3e} mean_abs={mean:.3e}", flush=True)
+    print(f"    long o (bf16 out) vs exact: max_abs={mx:.3e} mean_abs={mean:.3e} "
+          f"(mean bar {BF16_MEAN_ABS} not applied: bf16 storage alone costs ~8.6e-4)", flush=True)
     assert mx <= BF16_MAX_ABS
-    ref_b = inputs.bf16_bits_to_f32(inputs.f32_to_bf16_bits(ref.astype(np.float32)))
-    mx_b, mean_b = err_stats(take_rows(to_np(ob), p.rows), ref_b)
-    print(f"    long o (bf16 out) vs bf16-rounded exact: max_abs={mx_b:.3e} mean_abs={mean_b:.3e}", flush=True)
-    assert mean_b <= BF16_MEAN_ABS
 
 
 def test_two_stage_prefill_equals_one_call(lib):

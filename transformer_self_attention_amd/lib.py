@@ -148,11 +148,66 @@ def _win(window) -> int:
     return int(window)
 
 
-def _need(t: torch.Tensor, name: str):
+def _need(t: torch.Tensor, name: str, device=None):
     if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _shape(t: torch.Tensor, shape, name: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _table(table, D: int, device) -> int:
+    """Checks a RoPE coefficient table, float32 [max_pos, D/2, 2], and returns max_pos (0 for None:
+    no RoPE).  The C ABI receives only the row count, so the inner shape is checked here."""
+    if table is None:
+        return 0
+    _need(table, "table", device)
+    if table.dtype != torch.float32 or table.dim() != 3 or tuple(table.shape[1:]) != (D // 2, 2):
+        raise ValueError(f"table must be float32 [max_pos, {D // 2}, 2] for head dim {D}, "
+                         f"got {table.dtype} {tuple(table.shape)}")
+    return int(table.shape[0])
+
+
+def _out(out, shape, dtype, device):
+    """The output tensor: allocated when None, otherwise checked against the shape and device the
+    kernels will write (an undersized buffer would be written past its end)."""
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _need(out, "out", device)
+    _shape(out, shape, "out")
+    if dtype is not None and out.dtype != dtype:
+        raise ValueError(f"out has dtype {out.dtype}, expected {dtype}")
+    return out
+
+
+def _lse(lse, n: int, device):
+    if lse is None:
+        return
+    _need(lse, "lse", device)
+    if lse.dtype != torch.float32 or lse.numel() != n:
+        raise ValueError(f"lse must be float32 with {n} elements, got {lse.dtype} with {lse.numel()}")
+
+
+def _scratch(workspace, nbytes: int, device, stream):
+    """A caller's workspace (checked) or a new one.  A new one is tied to the stream the kernels run
+    on, so the allocator does not hand its memory out again while they may still use it."""
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+        if stream is not None:
+            workspace.record_stream(stream)
+        return workspace
+    _need(workspace, "workspace", device)
+    return workspace
+
+
+def _nbytes(t) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def rope_table_bytes(max_pos: int, D: int) -> int:
@@ -192,20 +247,33 @@ def make_rope_table(max_pos: int, D: int, base: float = 10000.0, device="cuda", 
 def rope_apply(x: torch.Tensor, table: torch.Tensor, pos0: int = 0, out: torch.Tensor = None, stream=None):
     """Rotate x [B, H, S, D] at positions pos0 + s (out=None: new tensor; out=x: in place)."""
     _need(x, "x")
-    _need(table, "table")
+    if x.dim() != 4:
+        raise ValueError("x must be [B, H, S, D]")
     B, H, S, D = x.shape
-    if out is None:
-        out = torch.empty_like(x)
-    _need(out, "out")
-    if out.shape != x.shape or out.dtype != x.dtype:
-        raise ValueError("out must match x")
-    _check(_lib.attn_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, S, D, pos0, _ptr(table),
-                                table.shape[0], _stream(stream)), "attn_rope_apply")
+    tmax = _table(table, D, x.device)
+    if tmax == 0:
+        raise ValueError("rope_apply needs a table")
+    out = x if out is x else _out(out, x.shape, x.dtype, x.device)
+    _check(_lib.attn_rope_apply(_ptr(x), _ptr(out), _dt(x), B, H, S, D, pos0, _ptr(table), tmax,
+                                _stream(stream)), "attn_rope_apply")
     return out
 
 
 def prefill_workspace_bytes(B, Hkv, S, D) -> int:
     return int(_lib.attn_prefill_workspace_bytes(B, Hkv, S, D))
+
+
+def _qkv(q, k, v):
+    """Shapes of a prefill's q [B, Hq, S, D] and k, v [B, Hkv, S, D], all on q's device."""
+    _need(q, "q")
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k and v must be [B, H, S, D]")
+    B, Hq, S, D = q.shape
+    Hkv = k.shape[1]
+    for t, n in ((k, "k"), (v, "v")):
+        _need(t, n, q.device)
+        _shape(t, (B, Hkv, S, D), n)
+    return B, Hq, Hkv, S, D
 
 
 def prefill(q, k, v, table=None, *, causal=True, pos0=0, window=None, out=None, out_dtype=None, lse=None,
@@ -216,32 +284,17 @@ def prefill(q, k, v, table=None, *, causal=True, pos0=0, window=None, out=None, 
 
     workspace: optional uint8 GPU tensor of >= prefill_workspace_bytes() bytes; with it the keys
     are rotated once into it (bf16 input with RoPE), without it the rotation is fused per tile."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
-    B, Hq, S, D = q.shape
-    Hkv = k.shape[1]
-    if k.shape != (B, Hkv, S, D) or v.shape != k.shape:
-        raise ValueError("k and v must be [B, Hkv, S, D] matching q")
+    B, Hq, Hkv, S, D = _qkv(q, k, v)
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise ValueError("q, k, v must share a dtype")
-    if out is None:
-        out = torch.empty((B, Hq, S, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    if lse is not None:
-        _need(lse, "lse")
-        if lse.dtype != torch.float32 or lse.numel() != B * Hq * S:
-            raise ValueError("lse must be float32 [B, Hq, S]")
-    tmax = 0
-    if table is not None:
-        _need(table, "table")
-        tmax = table.shape[0]
-    wsb = 0
+    out = _out(out, (B, Hq, S, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * S, q.device)
+    tmax = _table(table, D, q.device)
     if workspace is not None:
-        _need(workspace, "workspace")
-        wsb = workspace.numel() * workspace.element_size()
+        _need(workspace, "workspace", q.device)
     _check(_lib.attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq,
                              Hkv, S, D, 1 if causal else 0, pos0, _win(window), _ptr(table), tmax,
-                             _ptr(workspace), wsb, _stream(stream)),
+                             _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "attn_prefill")
     return out
 
@@ -249,16 +302,16 @@ def prefill(q, k, v, table=None, *, causal=True, pos0=0, window=None, out=None, 
 def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
     """Rotated keys as fp16 (a torch.float16 tensor shaped like k), for prefill_prerotated."""
     _need(k, "k")
-    _need(table, "table")
+    if k.dim() != 4:
+        raise ValueError("k must be [B, Hkv, S, D]")
     B, Hkv, S, D = k.shape
     if k.dtype != torch.bfloat16:
         raise TypeError("k must be bfloat16")
-    if out is None:
-        out = torch.empty(k.shape, dtype=torch.float16, device=k.device)
-    _need(out, "out")
-    if out.dtype != torch.float16 or out.shape != k.shape:
-        raise ValueError("out must be float16 shaped like k")
-    _check(_lib.attn_rotate_keys_f16(_ptr(k), _ptr(out), B, Hkv, S, D, pos0, _ptr(table), table.shape[0],
+    tmax = _table(table, D, k.device)
+    if tmax == 0:
+        raise ValueError("rotate_keys_f16 needs a table")
+    out = _out(out, k.shape, torch.float16, k.device)
+    _check(_lib.attn_rotate_keys_f16(_ptr(k), _ptr(out), B, Hkv, S, D, pos0, _ptr(table), tmax,
                                      _stream(stream)), "attn_rotate_keys_f16")
     return out
 
@@ -266,23 +319,34 @@ def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
 def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, window=None, out=None, out_dtype=None,
                        lse=None, stream=None):
     """prefill() for keys already rotated by rotate_keys_f16 (same table and pos0)."""
-    for t, n in ((q, "q"), (k_rot, "k_rot"), (v, "v"), (table, "table")):
-        _need(t, n)
-    B, Hq, S, D = q.shape
-    Hkv = k_rot.shape[1]
+    B, Hq, Hkv, S, D = _qkv(q, k_rot, v)
     if k_rot.dtype != torch.float16 or q.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
         raise TypeError("q, v bfloat16 and k_rot float16 expected")
-    if k_rot.shape != (B, Hkv, S, D) or v.shape != k_rot.shape:
-        raise ValueError("k_rot and v must be [B, Hkv, S, D] matching q")
-    if out is None:
-        out = torch.empty((B, Hq, S, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    if lse is not None:
-        _need(lse, "lse")
+    tmax = _table(table, D, q.device)
+    if tmax == 0:
+        raise ValueError("prefill_prerotated needs a table")
+    out = _out(out, (B, Hq, S, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * S, q.device)
     _check(_lib.attn_prefill_prerotated(_ptr(q), _ptr(k_rot), _ptr(v), _ptr(out), _ptr(lse), _dt(out), B, Hq,
                                         Hkv, S, D, 1 if causal else 0, pos0, _win(window), _ptr(table),
-                                        table.shape[0], _stream(stream)), "attn_prefill_prerotated")
+                                        tmax, _stream(stream)), "attn_prefill_prerotated")
     return out
+
+
+def _chunk_inputs(q, k_new, v_new):
+    """Shapes of a chunk's q [B, Hq, Sq, D] and k_new, v_new [B, Hkv, Sq, D] (all bf16)."""
+    _need(q, "q")
+    if q.dim() != 4 or k_new.dim() != 4:
+        raise ValueError("q, k_new and v_new must be [B, H, Sq, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv = k_new.shape[1]
+    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, q.device)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+    _shape(k_new, (B, Hkv, Sq, D), "k_new")
+    _shape(v_new, (B, Hkv, Sq, D), "v_new")
+    return B, Hq, Hkv, Sq, D
 
 
 def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, window=None, out=None,
@@ -293,42 +357,51 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, window
 
     workspace: uint8 GPU tensor of >= prefill_workspace_bytes(B, Hkv, pos0 + Sq, D) bytes, needed
     with RoPE; allocated here when None."""
-    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_cache, "k_cache"), (v_cache, "v_cache")):
-        _need(t, n)
+    B, Hq, Hkv, Sq, D = _chunk_inputs(q, k_new, v_new)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, S_max, D]")
+    S_max = k_cache.shape[2]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, q.device)
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{n} must be bfloat16")
-    B, Hq, Sq, D = q.shape
-    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
-    if k_new.shape != (B, Hkv, Sq, D) or v_new.shape != k_new.shape:
-        raise ValueError("k_new and v_new must be [B, Hkv, Sq, D]")
-    if k_cache.shape != (B, Hkv, S_max, D) or v_cache.shape != k_cache.shape:
-        raise ValueError("k_cache and v_cache must be [B, Hkv, S_max, D]")
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    if lse is not None:
-        _need(lse, "lse")
-        if lse.dtype != torch.float32 or lse.numel() != B * Hq * Sq:
-            raise ValueError("lse must be float32 [B, Hq, Sq]")
-    tmax = 0
-    if table is not None:
-        _need(table, "table")
-        tmax = table.shape[0]
-        if workspace is None:
-            workspace = torch.empty(max(prefill_workspace_bytes(B, Hkv, pos0 + Sq, D), 16), dtype=torch.uint8,
-                                    device=q.device)
-    wsb = 0
-    if workspace is not None:
-        _need(workspace, "workspace")
-        wsb = workspace.numel() * workspace.element_size()
+        _shape(t, (B, Hkv, S_max, D), n)
+    out = _out(out, (B, Hq, Sq, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * Sq, q.device)
+    tmax = _table(table, D, q.device)
+    if tmax:
+        workspace = _scratch(workspace, prefill_workspace_bytes(B, Hkv, pos0 + Sq, D), q.device, stream)
+    elif workspace is not None:
+        _need(workspace, "workspace", q.device)
     _check(_lib.attn_prefill_chunk(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                    _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _win(window), _ptr(table),
-                                   tmax, _ptr(workspace), wsb, _stream(stream)), "attn_prefill_chunk")
+                                   tmax, _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "attn_prefill_chunk")
     return out
 
 
 def prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D) -> int:
     return int(_lib.attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D))
+
+
+def _pool(k_pages, v_pages, Hkv, D, device):
+    """A paged pool [num_blocks, Hkv, block_size, D] (bf16) for K and V; returns (num_blocks, bs)."""
+    if k_pages.dim() != 4:
+        raise ValueError("k_pages must be [num_blocks, Hkv, block_size, D]")
+    num_blocks, bs = k_pages.shape[0], k_pages.shape[2]
+    for t, n in ((k_pages, "k_pages"), (v_pages, "v_pages")):
+        _need(t, n, device)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+        _shape(t, (num_blocks, Hkv, bs, D), n)
+    return num_blocks, bs
+
+
+def _block_table(block_table, B, device):
+    _need(block_table, "block_table", device)
+    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
+        raise ValueError(f"block_table must be int32 [{B}, max_blocks]")
+    return int(block_table.shape[1])
 
 
 def prefill_chunk_paged(q, k_new, v_new, k_pages, v_pages, block_table, pos0, table=None, *, window=None,
@@ -337,41 +410,18 @@ def prefill_chunk_paged(q, k_new, v_new, k_pages, v_pages, block_table, pos0, ta
     block table [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size]).
     The chunk's keys and values go into their blocks; workspace: uint8 GPU tensor of
     >= prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D) bytes, allocated here when None."""
-    for t, n in ((q, "q"), (k_new, "k_new"), (v_new, "v_new"), (k_pages, "k_pages"), (v_pages, "v_pages")):
-        _need(t, n)
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{n} must be bfloat16")
-    _need(block_table, "block_table")
-    if block_table.dtype != torch.int32 or block_table.dim() != 2:
-        raise ValueError("block_table must be int32 [B, max_blocks]")
-    B, Hq, Sq, D = q.shape
-    num_blocks, Hkv, bs = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
-    if k_new.shape != (B, Hkv, Sq, D) or v_new.shape != k_new.shape:
-        raise ValueError("k_new and v_new must be [B, Hkv, Sq, D]")
-    if k_pages.shape != (num_blocks, Hkv, bs, D) or v_pages.shape != k_pages.shape:
-        raise ValueError("k_pages and v_pages must be [num_blocks, Hkv, block_size, D]")
-    if block_table.shape[0] != B:
-        raise ValueError("block_table must have one row per sequence")
-    if out is None:
-        out = torch.empty((B, Hq, Sq, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    if lse is not None:
-        _need(lse, "lse")
-        if lse.dtype != torch.float32 or lse.numel() != B * Hq * Sq:
-            raise ValueError("lse must be float32 [B, Hq, Sq]")
-    tmax = 0
-    if table is not None:
-        _need(table, "table")
-        tmax = table.shape[0]
-    if workspace is None:
-        workspace = torch.empty(max(prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D), 16),
-                                dtype=torch.uint8, device=q.device)
-    _need(workspace, "workspace")
+    B, Hq, Hkv, Sq, D = _chunk_inputs(q, k_new, v_new)
+    num_blocks, bs = _pool(k_pages, v_pages, Hkv, D, q.device)
+    max_blocks = _block_table(block_table, B, q.device)
+    out = _out(out, (B, Hq, Sq, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * Sq, q.device)
+    tmax = _table(table, D, q.device)
+    workspace = _scratch(workspace, prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D), q.device, stream)
     _check(_lib.attn_prefill_chunk_paged(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
-                                         num_blocks, bs, _ptr(block_table), block_table.shape[1], _ptr(out),
+                                         num_blocks, bs, _ptr(block_table), max_blocks, _ptr(out),
                                          _ptr(lse), _dt(out), B, Hq, Hkv, Sq, D, pos0, _win(window), _ptr(table),
-                                         tmax, _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                         _stream(stream)), "attn_prefill_chunk_paged")
+                                         tmax, _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "attn_prefill_chunk_paged")
     return out
 
 
@@ -383,38 +433,45 @@ def decode_num_splits(B, Hq, Hkv, S_max, D, n_split=0) -> int:
     return int(_lib.attn_decode_num_splits(B, Hq, Hkv, S_max, D, n_split))
 
 
+def _decode_common(q, cache_len, q_pos):
+    """Shapes of a decode's q [B, Hq, 1, D] and its per-sequence int32 [B] vectors."""
+    _need(q, "q")
+    if q.dim() != 4 or q.shape[2] != 1:
+        raise ValueError("q must be [B, Hq, 1, D]")
+    B, Hq, _, D = q.shape
+    for t, n in ((cache_len, "cache_len"), (q_pos, "q_pos")):
+        if t is None:
+            if n == "cache_len":
+                raise ValueError("cache_len is required")
+            continue
+        _need(t, n, q.device)
+        if t.dtype != torch.int32 or t.numel() != B:
+            raise ValueError(f"{n} must be int32 [{B}]")
+    return B, Hq, D
+
+
 def decode(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, window=None, out=None,
            out_dtype=None, lse=None, workspace=None, stream=None):
     """One query per sequence (q [B, Hq, 1, D]) against the cache [B, Hkv, S_max, D].
 
     window: None, or W >= 0: only cache rows j >= q_pos[b] - W are seen."""
-    for t, n in ((q, "q"), (k_cache, "k_cache"), (v_cache, "v_cache"), (cache_len, "cache_len")):
-        _need(t, n)
-    B, Hq, one, D = q.shape
-    if one != 1:
-        raise ValueError("q must be [B, Hq, 1, D]")
+    B, Hq, D = _decode_common(q, cache_len, q_pos)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, S_max, D]")
     Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
-    if cache_len.dtype != torch.int32 or cache_len.numel() != B:
-        raise ValueError("cache_len must be int32 [B]")
-    if q_pos is not None:
-        _need(q_pos, "q_pos")
-        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
-            raise ValueError("q_pos must be int32 [B]")
-    if out is None:
-        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    need = decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _need(workspace, "workspace")
-    tmax = 0
-    if table is not None:
-        _need(table, "table")
-        tmax = table.shape[0]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, q.device)
+        _shape(t, (B, Hkv, S_max, D), n)
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} must have q's dtype")
+    out = _out(out, (B, Hq, 1, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq, q.device)
+    tmax = _table(table, D, q.device)
+    workspace = _scratch(workspace, decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split), q.device, stream)
     _check(_lib.attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(q_pos),
                             _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _win(window),
-                            _ptr(table), tmax, n_split, _ptr(workspace),
-                            workspace.numel() * workspace.element_size(), _stream(stream)), "attn_decode")
+                            _ptr(table), tmax, n_split, _ptr(workspace), _nbytes(workspace), _stream(stream)),
+           "attn_decode")
     return out
 
 
@@ -422,38 +479,22 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None,
                  out=None, out_dtype=None, lse=None, workspace=None, stream=None):
     """decode() against a paged cache: pools [num_blocks, Hkv, block_size, D] and an int32 block
     table [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size])."""
-    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"), (block_table, "block_table"),
-                 (cache_len, "cache_len")):
-        _need(t, n)
-    B, Hq, one, D = q.shape
-    if one != 1:
-        raise ValueError("q must be [B, Hq, 1, D]")
-    num_blocks, Hkv, bs, _ = k_pages.shape
-    if v_pages.shape != k_pages.shape:
-        raise ValueError("k_pages and v_pages must match")
-    if block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.shape[0] != B:
-        raise ValueError("block_table must be int32 [B, max_blocks]")
-    max_blocks = block_table.shape[1]
-    if cache_len.dtype != torch.int32 or cache_len.numel() != B:
-        raise ValueError("cache_len must be int32 [B]")
-    if q_pos is not None:
-        _need(q_pos, "q_pos")
-        if q_pos.dtype != torch.int32 or q_pos.numel() != B:
-            raise ValueError("q_pos must be int32 [B]")
-    if out is None:
-        out = torch.empty((B, Hq, 1, D), dtype=out_dtype or q.dtype, device=q.device)
-    _need(out, "out")
-    need = decode_workspace_bytes(B, Hq, Hkv, max_blocks * bs, D, n_split)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
-    _need(workspace, "workspace")
-    tmax = 0
-    if table is not None:
-        _need(table, "table")
-        tmax = table.shape[0]
+    B, Hq, D = _decode_common(q, cache_len, q_pos)
+    if k_pages.dim() != 4:
+        raise ValueError("k_pages must be [num_blocks, Hkv, block_size, D]")
+    Hkv = k_pages.shape[1]
+    num_blocks, bs = _pool(k_pages, v_pages, Hkv, D, q.device)
+    if k_pages.dtype != q.dtype:
+        raise ValueError("k_pages must have q's dtype")
+    max_blocks = _block_table(block_table, B, q.device)
+    out = _out(out, (B, Hq, 1, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq, q.device)
+    tmax = _table(table, D, q.device)
+    workspace = _scratch(workspace, decode_workspace_bytes(B, Hq, Hkv, max_blocks * bs, D, n_split), q.device,
+                         stream)
     _check(_lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), num_blocks, bs, _ptr(block_table),
                                   max_blocks, _ptr(cache_len), _ptr(q_pos), _ptr(out), _ptr(lse), _dt(q), _dt(out),
                                   B, Hq, Hkv, D, _win(window), _ptr(table), tmax, n_split, _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)),
+                                  _nbytes(workspace), _stream(stream)),
            "attn_decode_paged")
     return out
