@@ -26,7 +26,7 @@
  *   - Tensors are dense, row-major ("C order") [B, H, S, D] with D innermost, on the
  *     device.  Every tensor pointer must be 16-byte aligned.
  *   - The caller owns all memory.  The library allocates nothing, keeps no state between
- *     calls, never synchronises, and enqueues its kernels on `stream` (a hipStream_t;
+ *     calls (attn_decode_noalloc's static buffer aside), never synchronises, and enqueues its kernels on `stream` (a hipStream_t;
  *     NULL means the default stream).  Calls are asynchronous: a returned ATTN_OK means
  *     the work was enqueued.
  *   - Only kernel launches reach the stream (no memset, copy or event), so a call made
@@ -34,7 +34,8 @@
  *     replayed; its buffers must then stay allocated for as long as the graph is used.
  *   - Every argument that can be checked on the host is checked before any HIP call; a
  *     rejected call enqueues nothing.  HIP launch errors map to ATTN_ERR_HIP.
- *   - No C++ exception crosses this interface.  Calls are thread-safe (no shared state).
+ *   - No C++ exception crosses this interface.  Calls are thread-safe (no shared state),
+ *     except attn_decode_noalloc, whose calls on one GPU share that GPU's static buffer.
  *   - window (every attention entry point): a negative value means no window.  window = W >= 0
  *     is a sliding window ("Building Self-Attention and Transformer Engines",
  *     codingpancake.com, section 6.4: each token attends only to the W tokens before it): the
@@ -275,6 +276,32 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
                         int D, int window, const float* rope_table, int table_max_pos, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_decode_noalloc: attn_decode for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, serving loops that must not allocate, harnesses that forbid it.
+ *
+ * Arguments, results and the support matrix are attn_decode's, without the workspace: the
+ * partial results of the cache splits go to a buffer inside the library, a static device array
+ * of ATTN_NOALLOC_SCRATCH_BYTES (16 MiB) on each GPU, created when the library's code object is
+ * loaded on that GPU and held until the process ends.  The call allocates nothing (no hipMalloc,
+ * no allocator of any kind) and enqueues only kernel launches.  No part of the buffer needs to
+ * start at zero: every partial the merge pass reads is written earlier in the same call.
+ * Every call on one GPU uses that GPU's one buffer, so two calls that can overlap on the same GPU
+ * (issued on different streams, or from different threads without ordering) race and corrupt
+ * each other's results; the caller must order them.
+ * Errors: those of attn_decode (except the workspace checks); ATTN_ERR_UNSUPPORTED when the
+ * partials need more than the buffer holds, i.e. when attn_decode_workspace_bytes(B, Hq, Hkv,
+ * S_max, D, n_split) > ATTN_NOALLOC_SCRATCH_BYTES (for example B = 32, Hq = 64, Hkv = 1,
+ * 8192 keys needs 8.5 MB with the automatic split count); ATTN_ERR_HIP when the buffer's device
+ * address cannot be obtained or the launch fails.
+ * --------------------------------------------------------------------------------------- */
+#define ATTN_NOALLOC_SCRATCH_BYTES (16u << 20)
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                                attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max, int D,
+                                int window, const float* rope_table, int table_max_pos, int n_split,
+                                void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_decode_paged: attn_decode against a paged KV cache.  The cache is a pool of

@@ -269,3 +269,33 @@ def _paged(**kw):
 ])
 def test_decode_paged_rejects(kw, code):
     assert _paged(**kw) == code
+
+
+def _decode_noalloc(**kw):
+    a = dict(q=A, kc=A, vc=A, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16, B=4, Hq=16, Hkv=2,
+             S=1000, D=128, window=-1, table=A, tmax=2000, ns=0, stream=None)
+    a.update(kw)
+    return lib.raw().attn_decode_noalloc(a["q"], a["kc"], a["vc"], a["cl"], a["qp"], a["o"], a["lse"],
+                                         a["in_dt"], a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"],
+                                         a["window"], a["table"], a["tmax"], a["ns"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kc=None), INV), (dict(cl=None), INV), (dict(o=None), INV), (dict(qp=None), INV),
+    (dict(B=0), INV), (dict(Hq=15), INV), (dict(ns=-1), INV), (dict(kc=MIS), INV), (dict(lse=MIS), INV),
+    (dict(table=MIS), INV), (dict(in_dt=F32), UNSUP), (dict(D=96), UNSUP),
+    # partials beyond the static buffer: 32 x 64 query heads x 64 splits x (128 + 2) floats = 68 MB
+    (dict(B=32, Hq=64, Hkv=1, S=8192, ns=64), UNSUP),
+    (dict(B=4096, Hq=64, Hkv=8, S=8192, ns=2), UNSUP),
+])
+def test_decode_noalloc_rejects(kw, code):
+    """Rejected on the host before the buffer's address is looked up or anything is launched."""
+    assert _decode_noalloc(**kw) == code
+
+
+def test_decode_noalloc_buffer_bound():
+    """The multi-query decode config fits the buffer with the automatic split count; 64 splits do not."""
+    assert lib.NOALLOC_SCRATCH_BYTES == 16 << 20
+    need = lib.decode_workspace_bytes(32, 64, 1, 8192, 128, 0)
+    assert need == 32 * 64 * 8 * 130 * 4 <= lib.NOALLOC_SCRATCH_BYTES
+    assert lib.decode_workspace_bytes(32, 64, 1, 8192, 128, 64) > lib.NOALLOC_SCRATCH_BYTES

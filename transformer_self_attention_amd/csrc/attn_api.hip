@@ -6,6 +6,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "common.h"
 
@@ -65,6 +66,81 @@ void decode_geometry(int B, int Hq, int Hkv, int S_max, int n_split_req, int* n_
   if (ns_eff < 1) ns_eff = 1;
   *n_split = ns_eff;
   *chunk = c;
+}
+
+// Host checks of attn_decode's arguments other than the workspace.
+attn_status check_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* cache_len,
+                         const int32_t* q_pos, const void* o, const float* lse, attn_dtype in_dt,
+                         attn_dtype out_dt, int B, int Hq, int Hkv, int S_max, int D, int window,
+                         const float* rope_table, int table_max_pos, int n_split) {
+  if (!q || !k_cache || !v_cache || !cache_len || !o) return ATTN_ERR_INVALID_ARG;
+  if ((rope_table || window >= 0) && !q_pos) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
+      (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) ||
+      (q_pos && (reinterpret_cast<uintptr_t>(q_pos) & 3u)))
+    return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (!aligned16(rope_table) || table_max_pos < 1)) return ATTN_ERR_INVALID_ARG;
+  return ATTN_OK;
+}
+
+// Host checks that follow the workspace check (the support matrix).
+attn_status check_decode_support(attn_dtype in_dt, int B, int Hkv, int S_max, int D) {
+  if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * S_max * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+  return ATTN_OK;
+}
+
+hipError_t launch_decode_contiguous(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                                    attn_dtype out_dt, int B, int Hq, int Hkv, int S_max, int D, int window,
+                                    const float* rope_table, int table_max_pos, int n_split, void* workspace,
+                                    hipStream_t st) {
+  int ns, chunk;
+  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
+  attn::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache;
+  a.cache_len = cache_len; a.q_pos = q_pos;
+  a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_max = S_max; a.D = D;
+  a.table = rope_table; a.table_max_pos = table_max_pos;
+  a.n_split = ns; a.chunk = chunk;
+  const size_t parts = (size_t)B * Hq * ns;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = static_cast<float*>(workspace) + parts * D;
+  a.block_table = nullptr;
+  a.max_blocks = 0; a.bs_log2 = 0; a.num_blocks = 0;
+  a.window = kernel_window(window);
+  return attn::launch_decode(a, st);
+}
+
+// ---- the static scratch buffer of attn_decode_noalloc --------------------------------------
+// One copy per GPU, allocated when the code object is loaded and held until the process ends.
+// In host code `scratch` is only the runtime's handle for the symbol: its device address, which
+// differs per GPU, is looked up once per device and used everywhere instead.
+static_assert(ATTN_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[ATTN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's copy of `scratch` (nullptr on a HIP error).
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -328,40 +404,37 @@ attn_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
                         attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max,
                         int D, int window, const float* rope_table, int table_max_pos, int n_split,
                         void* workspace, size_t workspace_bytes, void* stream) {
-  if (!q || !k_cache || !v_cache || !cache_len || !o || !workspace) return ATTN_ERR_INVALID_ARG;
-  if ((rope_table || window >= 0) && !q_pos) return ATTN_ERR_INVALID_ARG;
-  if (!valid_dtype(in_dt) || !valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
-  if (B < 1 || Hq < 1 || Hkv < 1 || S_max < 1 || D < 1 || n_split < 0) return ATTN_ERR_INVALID_ARG;
-  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
-  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o) ||
-      !aligned16(workspace) || (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(cache_len) & 3u) ||
-      (q_pos && (reinterpret_cast<uintptr_t>(q_pos) & 3u)))
-    return ATTN_ERR_INVALID_ARG;
-  if (rope_table && (!aligned16(rope_table) || table_max_pos < 1)) return ATTN_ERR_INVALID_ARG;
+  attn_status s = check_decode(q, k_cache, v_cache, cache_len, q_pos, o, lse, in_dt, out_dt, B, Hq, Hkv, S_max,
+                               D, window, rope_table, table_max_pos, n_split);
+  if (s != ATTN_OK) return s;
+  if (!workspace || !aligned16(workspace)) return ATTN_ERR_INVALID_ARG;
   if (workspace_bytes < attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split))
     return ATTN_ERR_INVALID_ARG;
-  if (in_dt != ATTN_BF16) return ATTN_ERR_UNSUPPORTED;
-  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
-  if ((int64_t)B * Hkv * S_max * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+  s = check_decode_support(in_dt, B, Hkv, S_max, D);
+  if (s != ATTN_OK) return s;
+  return from_hip(launch_decode_contiguous(q, k_cache, v_cache, cache_len, q_pos, o, lse, out_dt, B, Hq, Hkv,
+                                           S_max, D, window, rope_table, table_max_pos, n_split, workspace,
+                                           (hipStream_t)stream));
+}
 
-  int ns, chunk;
-  decode_geometry(B, Hq, Hkv, S_max, n_split, &ns, &chunk);
-  attn::DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache;
-  a.cache_len = cache_len; a.q_pos = q_pos;
-  a.o = o; a.lse = lse;
-  a.out_bf16 = out_dt == ATTN_BF16;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S_max = S_max; a.D = D;
-  a.table = rope_table; a.table_max_pos = table_max_pos;
-  a.n_split = ns; a.chunk = chunk;
-  const size_t parts = (size_t)B * Hq * ns;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = static_cast<float*>(workspace) + parts * D;
-  a.block_table = nullptr;
-  a.max_blocks = 0; a.bs_log2 = 0; a.num_blocks = 0;
-  a.window = kernel_window(window);
-  return from_hip(attn::launch_decode(a, (hipStream_t)stream));
+attn_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* cache_len, const int32_t* q_pos, void* o, float* lse,
+                                attn_dtype in_dt, attn_dtype out_dt, int B, int Hq, int Hkv, int S_max, int D,
+                                int window, const float* rope_table, int table_max_pos, int n_split,
+                                void* stream) {
+  attn_status s = check_decode(q, k_cache, v_cache, cache_len, q_pos, o, lse, in_dt, out_dt, B, Hq, Hkv, S_max,
+                               D, window, rope_table, table_max_pos, n_split);
+  if (s != ATTN_OK) return s;
+  // the partials of every split must fit the static buffer
+  if (attn_decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split) > (size_t)ATTN_NOALLOC_SCRATCH_BYTES)
+    return ATTN_ERR_UNSUPPORTED;
+  s = check_decode_support(in_dt, B, Hkv, S_max, D);
+  if (s != ATTN_OK) return s;
+  void* ptr = scratch_on_current_device();
+  if (!ptr) return ATTN_ERR_HIP;
+  return from_hip(launch_decode_contiguous(q, k_cache, v_cache, cache_len, q_pos, o, lse, out_dt, B, Hq, Hkv,
+                                           S_max, D, window, rope_table, table_max_pos, n_split, ptr,
+                                           (hipStream_t)stream));
 }
 
 attn_status attn_decode_paged(const void* q, const void* k_pages, const void* v_pages, int num_blocks,

@@ -37,7 +37,10 @@ EXPORTED = (
     "attn_decode_num_splits",
     "attn_decode",
     "attn_decode_paged",
+    "attn_decode_noalloc",
 )
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ATTN_NOALLOC_SCRATCH_BYTES
 
 
 class AttnError(RuntimeError):
@@ -93,6 +96,9 @@ def _load():
     lib.attn_decode_paged.restype = i32
     lib.attn_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32,
                                       i32, fp, i32, i32, vp, sz, vp]
+    lib.attn_decode_noalloc.restype = i32
+    lib.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32, fp,
+                                        i32, i32, vp]
     return lib
 
 
@@ -497,4 +503,28 @@ def decode_paged(q, k_pages, v_pages, block_table, cache_len, q_pos, table=None,
                                   B, Hq, Hkv, D, _win(window), _ptr(table), tmax, n_split, _ptr(workspace),
                                   _nbytes(workspace), _stream(stream)),
            "attn_decode_paged")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, cache_len, q_pos, table=None, *, n_split=0, window=None, out=None,
+                   out_dtype=None, lse=None, stream=None):
+    """decode() through attn_decode_noalloc: the split partials go to the library's static per-GPU
+    buffer instead of a workspace, so the C call allocates nothing (out is allocated here when None).
+    Calls that can overlap on one GPU race on that buffer."""
+    B, Hq, D = _decode_common(q, cache_len, q_pos)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, S_max, D]")
+    Hkv, S_max = k_cache.shape[1], k_cache.shape[2]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, q.device)
+        _shape(t, (B, Hkv, S_max, D), n)
+        if t.dtype != q.dtype:
+            raise ValueError(f"{n} must have q's dtype")
+    out = _out(out, (B, Hq, 1, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq, q.device)
+    tmax = _table(table, D, q.device)
+    _check(_lib.attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_len), _ptr(q_pos),
+                                    _ptr(out), _ptr(lse), _dt(q), _dt(out), B, Hq, Hkv, S_max, D, _win(window),
+                                    _ptr(table), tmax, n_split, _stream(stream)),
+           "attn_decode_noalloc")
     return out
