@@ -140,36 +140,34 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // of row P / NCH.  The per-lane element offsets are fixed for the whole kernel; each tile adds
   // a wave-uniform base.  Rows past Sk read row Sk-1 (finite data; those keys are masked).
   // Byte offsets are unsigned 32-bit so the loads use the scalar-base + vector-offset form.
-  uint32_t dma_byte[DIRECT_PER_WAVE];
-  int dma_row[DIRECT_PER_WAVE];
-#pragma unroll
-  for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
-    const int P = (i * NW + wave) * 64 + lane;
-    const int r = P / NCH;
-    dma_row[i] = r;
-    dma_byte[i] = (uint32_t)(r * D + swz<D>(r, P % NCH) * 8) * 2u;
-  }
+  // Wave-load i of this wave fills LDS chunks [(i * NW + wave) * 64, +64): lane L's chunk P holds
+  // logical chunk swz(row, P % NCH) of row P / NCH.  Row r_i = r_0 + i * rows_per_load, and the
+  // swizzle sees only the low rows bits that i leaves unchanged, so the byte offset of load i is
+  // dma_base + i * load_bytes (passed as the load's scalar offset).  Rows past Sk (tail tile only)
+  // read row Sk-1 (finite data; those keys are masked).
+  constexpr int ROWS_PER_LOAD = NW * 64 / NCH;          // rows one round of wave-loads covers
+  constexpr uint32_t LOAD_BYTES = ROWS_PER_LOAD * D * 2;
+  static_assert(ROWS_PER_LOAD % 16 == 0 || (D == 64 && ROWS_PER_LOAD % 8 == 0), "swizzle period");
+  const int dma_r0 = (wave * 64 + lane) / NCH;
+  const uint32_t dma_base = (uint32_t)(dma_r0 * D + swz<D>(dma_r0, (wave * 64 + lane) % NCH) * 8) * 2u;
   auto direct_tile = [&](const uint16_t* src, uint16_t* dst_tile, int k0) {
-    // (operands are formed in locals first: the host compilation pass rejects captured-array
-    // elements inside the builtin's argument list and would silently drop the kernel)
     const char* base = reinterpret_cast<const char*>(src + (int64_t)k0 * D);
     if (k0 + kBN <= Sk) {
-      // full tile: a buffer resource over the tile (scalar work only) and the fixed per-lane
-      // offsets, so no per-lane address arithmetic is repeated per tile
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, kBN * D * 2, kBufferWord3);
 #pragma unroll
       for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
-        const uint32_t off = dma_byte[i];
         ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, l, 16, (int)off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, l, 16, (int)dma_base, (int)(LOAD_BYTES * i), 0, 0);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < DIRECT_PER_WAVE; ++i) {
-        const int r = dma_row[i];
+        // (the no-op keeps this address arithmetic in the tail branch: hoisted, it ran every tile)
+        int r = dma_r0 + ROWS_PER_LOAD * i;
+        asm volatile("" : "+v"(r));
         const int rr = min(r, Sk - 1 - k0);
-        const uint32_t off = dma_byte[i] - (uint32_t)((r - rr) * D * 2);
+        const uint32_t off = dma_base + LOAD_BYTES * i - (uint32_t)((r - rr) * D * 2);
         const void* g = base + off;
         ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
         __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
