@@ -61,11 +61,11 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 # for 1048576 KiB read (factor 2.0 applied), WRITE_SIZE reads 1048576 KiB (factor 1.0).
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (11 dispatches):
-    # FETCH_SIZE 160599.4 KiB, WRITE_SIZE 131072.0 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 463125245, "sources_sha256_16": "218bfa802c0363cc"},
+    # FETCH_SIZE 160579.2 KiB, WRITE_SIZE 131085.7 KiB per dispatch.
+    "prefill_gqa": {"bytes_per_launch": 463097999, "sources_sha256_16": "173859493f308006"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
-    # FETCH_SIZE 528564.7 KiB, WRITE_SIZE 512.0 KiB per step.
-    "decode": {"bytes_per_launch": 1083024752, "sources_sha256_16": "c953fb4373c29e42"},
+    # FETCH_SIZE 528498.7 KiB, WRITE_SIZE 512.0 KiB per step.
+    "decode": {"bytes_per_launch": 1082889696, "sources_sha256_16": "5d557da53e857dc5"},
 }
 KERNEL_SOURCES = {
     "prefill_gqa": ["transformer_self_attention_amd/csrc/prefill_bf16.hip",
@@ -139,7 +139,7 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True, out_dtype=None)
     tab = lib.make_rope_table(wl.S, wl.D)
     out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
     ws = torch.empty(lib.prefill_workspace_bytes(wl.B, wl.Hkv, wl.S, wl.D), dtype=torch.uint8, device="cuda")
-    krot = ws.view(torch.float16).view(k.shape)
+    krot = ws   # rotated fp16 keys, then their exponent bytes
     torch.cuda.synchronize()
     flops = wl.prefill_flops()
 

@@ -64,7 +64,8 @@ typedef enum {
   ATTN_BF16 = 1  /* bfloat16; results are rounded to nearest, ties to even */
 } attn_dtype;
 
-/* Version of this interface (major * 10000 + minor * 100 + patch). */
+/* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
+ * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys. */
 int attn_version(void);
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -139,16 +140,21 @@ attn_status attn_rope_apply(const void* x, void* out, attn_dtype dt, int B, int 
  * Scale: 1/sqrt(D), fixed.
  * workspace: optional device scratch of at least attn_prefill_workspace_bytes(B, Hkv, S, D)
  *      bytes (contents on entry irrelevant, overwritten).  Used only for bf16 input with RoPE:
- *      the keys are then rotated once, in one pass, into the workspace, and the attention
- *      kernel streams the rotated keys.  With workspace == NULL the key rotation is fused into
- *      every K tile load instead (same results; more arithmetic per tile).
+ *      the keys are then rotated once, in one pass, into the workspace (the layout of
+ *      attn_rotate_keys_f16), and the attention kernel streams the rotated keys.  With
+ *      workspace == NULL the key rotation is fused into every K tile load instead (same
+ *      results; more arithmetic per tile).
  *
  * Support matrix: D in {64, 128}; in_dt = ATTN_F32 (float32 arithmetic throughout, out_dt
  * must be ATTN_F32) or in_dt = ATTN_BF16 (out_dt either).  For bf16 input with RoPE the
- * rotated q and k are rounded to IEEE half precision for the Q.K^T matrix-core product
- * (fp32 accumulation), so |q|, |k| must stay below 4.6e4; without RoPE the bf16 inputs are
- * multiplied exactly.  The softmax weights are rounded to bf16 for the P.V product (fp32
- * accumulation).
+ * rotated q and k rows are rounded to IEEE half precision for the Q.K^T matrix-core product
+ * (fp32 accumulation).  A row whose largest magnitude reaches 2^15 (a query row after its
+ * scale log2(e)/sqrt(D)) is first multiplied by 2^-e, e the smallest non-negative integer
+ * that brings it below 2^15, and its products are multiplied by 2^e again in float32: every
+ * finite bf16 input has a result as accurate as for small rows, until a score itself leaves
+ * the float32 range.  Elements below 2^-14 after that scale are half-precision subnormals
+ * (absolute precision 2^-24).  Without RoPE the bf16 inputs are multiplied exactly.  The
+ * softmax weights are rounded to bf16 for the P.V product (fp32 accumulation).
  * Errors: ATTN_ERR_INVALID_ARG for null q/k/v/o, B/Hq/Hkv/S < 1, Hq % Hkv != 0, bad RoPE
  * range, a window without the causal mask, a workspace that is misaligned or too small,
  * misalignment; ATTN_ERR_UNSUPPORTED outside the support matrix.
@@ -163,11 +169,16 @@ attn_status attn_prefill(const void* q, const void* k, const void* v, void* o, f
  * The two stages of attn_prefill with a workspace, callable on their own (for example to
  * rotate a sequence's keys once and run several query batches against them).
  *
- * attn_rotate_keys_f16: k_rot[b,h,s,:] = RoPE(k[b,h,s,:]) at position pos0 + s, computed in
- *   float32 from bf16 k [B, Hkv, S, D] and stored as IEEE half precision (same layout).
+ * attn_rotate_keys_f16: key row r = RoPE(k[b,h,s,:]) at position pos0 + s, computed in
+ *   float32 from bf16 k [B, Hkv, S, D].  k_rot is a device buffer of at least
+ *   attn_prefill_workspace_bytes(B, Hkv, S, D) bytes, 16-byte aligned, owned by the caller:
+ *   it receives first IEEE half [B, Hkv, S, D] holding r * 2^-e, then one unsigned byte e per
+ *   row [B, Hkv, S], where e is the smallest non-negative integer with max |r| * 2^-e < 2^15
+ *   (0 for every row below 2^15, and for a row holding an infinity; inf and NaN elements are
+ *   stored as they are and propagate to the scores).
  * attn_prefill_prerotated: attn_prefill for bf16 q and v with RoPE, whose keys were already
- *   rotated by attn_rotate_keys_f16 with the same table and pos0 (k_rot is read as fp16 and
- *   never rotated again; q is rotated at pos0 + s).  Other arguments as in attn_prefill.
+ *   rotated by attn_rotate_keys_f16 with the same table and pos0 (k_rot is that buffer, read
+ *   and never rotated again; q is rotated at pos0 + s).  Other arguments as in attn_prefill.
  * Support matrix: D in {64, 128}.  Errors as in attn_prefill (rope_table is required).
  * --------------------------------------------------------------------------------------- */
 attn_status attn_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
@@ -198,8 +209,9 @@ attn_status attn_prefill_prerotated(const void* q, const void* k_rot, const void
  * rope_table: NULL disables RoPE (keys copied into the cache as given, Q.K^T on the exact
  *   bf16 values); otherwise requires pos0 + Sq <= table_max_pos.
  * workspace: required with RoPE: at least attn_prefill_workspace_bytes(B, Hkv, pos0 + Sq, D)
- *   bytes, 16-byte aligned, contents irrelevant.  It receives every key row [0, pos0 + Sq)
- *   as IEEE half, the Q.K^T operand format (so cached |k| must stay below 6.5e4).
+ *   bytes, 16-byte aligned, contents irrelevant.  It receives every key row [0, pos0 + Sq) in
+ *   the Q.K^T operand format of attn_rotate_keys_f16 (IEEE half with a per-row exponent, so
+ *   cached keys of any finite magnitude are handled as in attn_prefill).
  * k_new, v_new and q must not overlap the cache.  pos0 = 0 is an ordinary causal prefill whose
  * keys are kept.
  * Support matrix: D in {64, 128}; out_dt either.
@@ -231,7 +243,8 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
  *   may already have been released.
  * workspace: required, at least attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D)
  *   bytes, 16-byte aligned, contents irrelevant: it receives contiguous copies of the visible
- *   key rows (IEEE half with RoPE, bf16 without) and value rows.
+ *   key rows (with RoPE in the operand format of attn_rotate_keys_f16, bf16 without) and value
+ *   rows.
  * Other arguments, the support matrix and the errors as in attn_prefill_chunk; also
  * ATTN_ERR_INVALID_ARG for a bad block size, a null or misaligned block table, or a chunk
  * past the table.  Table entries outside [0, num_blocks) are clamped into it.

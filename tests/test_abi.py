@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lib.version() == 10000
+    assert lib.version() == 20000
     assert lib.status_string(OK) == "ATTN_OK"
     for s in (INV, UNSUP, lib.ATTN_ERR_HIP):
         assert lib.status_string(s).startswith("ATTN_ERR_")
@@ -155,7 +155,9 @@ def test_rope_table_init_rejects():
 
 
 def test_prefill_workspace_bytes():
-    assert lib.prefill_workspace_bytes(1, 8, 8192, 128) == 8 * 8192 * 128 * 2
+    # fp16 rotated keys, then one exponent byte per key row (rounded up to 256 bytes)
+    assert lib.prefill_workspace_bytes(1, 8, 8192, 128) == 8 * 8192 * 128 * 2 + 8 * 8192
+    assert lib.prefill_workspace_bytes(1, 1, 100, 64) == 100 * 64 * 2 + 256
     assert lib.prefill_workspace_bytes(0, 8, 8192, 128) == 0
 
 
@@ -222,7 +224,8 @@ def _chunk_paged(**kw):
 
 
 def test_prefill_chunk_paged_workspace_bytes():
-    assert lib.prefill_chunk_paged_workspace_bytes(1, 8, 6144, 2048, 128) == 2 * 8 * 8192 * 128 * 2
+    # keys (fp16) and their exponent bytes, then the values (bf16)
+    assert lib.prefill_chunk_paged_workspace_bytes(1, 8, 6144, 2048, 128) == 2 * 8 * 8192 * 128 * 2 + 8 * 8192
     assert lib.prefill_chunk_paged_workspace_bytes(0, 8, 0, 10, 128) == 0
     assert lib.prefill_chunk_paged_workspace_bytes(1, 8, -1, 10, 128) == 0
 

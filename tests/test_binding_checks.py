@@ -91,15 +91,20 @@ def test_prefill_rejects_before_launch(stub, kw):
 
 def test_prerotated_and_rotation_reject_before_launch(stub):
     q, v = T(1, 8, 64, 128), T(1, 2, 64, 128)
-    kr = T(1, 2, 64, 128, dtype=torch.float16)
+    need = lib.prefill_workspace_bytes(1, 2, 64, 128)       # the stub answers 1 MiB
+    kr = T(need, dtype=torch.uint8)
     tab = table(64, 128)
     for kw in (dict(out=T(1, 8, 64, 127)), dict(lse=T(3, dtype=f32)), dict()):
         with pytest.raises(ValueError):
             lib.prefill_prerotated(q, kr, v, tab if kw else table(64, 64), **kw)
+    with pytest.raises(ValueError):                          # keys buffer one byte short
+        lib.prefill_prerotated(q, T(need - 1, dtype=torch.uint8), v, tab)
+    with pytest.raises(ValueError):                          # not a byte buffer
+        lib.prefill_prerotated(q, T(1, 2, 64, 128, dtype=torch.float16), v, tab)
     with pytest.raises(ValueError):
-        lib.rotate_keys_f16(v, tab, out=T(1, 2, 64, 128))               # out must be fp16
+        lib.rotate_keys_f16(v, tab, out=T(1, 2, 64, 128))               # out must be uint8
     with pytest.raises(ValueError):
-        lib.rotate_keys_f16(v, tab, out=T(1, 2, 32, 128, dtype=torch.float16))
+        lib.rotate_keys_f16(v, tab, out=T(need - 1, dtype=torch.uint8))
     with pytest.raises(ValueError):
         lib.rope_apply(q, tab, out=T(1, 8, 64, 64))
     with pytest.raises(ValueError):

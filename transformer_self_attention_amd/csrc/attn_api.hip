@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 10000;  // 1.0.0
+constexpr int kVersion = 20000;  // 2.0.0
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -328,7 +328,8 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
 
 size_t attn_prefill_chunk_paged_workspace_bytes(int B, int Hkv, int pos0, int Sq, int D) {
   if (B < 1 || Hkv < 1 || pos0 < 0 || Sq < 1 || D < 1) return 0;
-  return 2 * attn::prefill_workspace_bytes(B, Hkv, pos0 + Sq, D);
+  // the keys (with their exponent bytes) of the visible rows, then their values
+  return attn::prefill_workspace_bytes(B, Hkv, pos0 + Sq, D) + attn::prefill_kexp_offset(B, Hkv, pos0 + Sq, D);
 }
 
 attn_status attn_prefill_chunk_paged(const void* q, const void* k_new, const void* v_new, void* k_pages,

@@ -12,8 +12,11 @@
 //    to bf16 (nearest even) into the cache; the value is copied;
 //  * with RoPE the attention kernel multiplies fp16 operands, so every key row [0, pos0+Sq) is
 //    also written to k16 [B*Hkv, pos0+Sq, D] as fp16: the earlier rows converted from the cache,
-//    the new rows from the very bf16 values just stored (bf16 -> fp16 is exact for
-//    6.1e-5 <= |x| <= 65504; smaller magnitudes round to fp16's subnormal grid, 2^-24).
+//    the new rows from the very bf16 values just stored, each row scaled by 2^-e with its
+//    exponent byte e in kexp [B*Hkv, pos0+Sq] (f16_row_exponent: e = 0 unless the row reaches
+//    2^15; bf16 -> fp16 is then exact for 6.1e-5 <= |x|, smaller magnitudes round to fp16's
+//    subnormal grid, 2^-24).  The NCH lanes of one row are consecutive, so a row's maximum is a
+//    group reduction.
 //
 // Paged cache (cache_append_paged_kernel): the pool [num_blocks, Hkv, bs, D] and block table of
 // codingpancake.com "Building Self-Attention and Transformer Engines", section 6.2; token t of
@@ -29,11 +32,25 @@ namespace attn {
 
 namespace {
 
+// A key row segment of 8 bf16 values (one lane's 16 bytes) as fp16 scaled by 2^-e, e the exponent
+// of the whole row (its NCH lanes together); returns e.
+template <int NCH>
+__device__ __forceinline__ int to_f16_row(const u32x4 w, u32x4& h) {
+  float mx = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) mx = fmaxf(mx, fmaxf(fabsf(bf16lo(w[t])), fabsf(bf16hi(w[t]))));
+  const int e = f16_row_exponent(group_max<NCH>(mx));
+#pragma unroll
+  for (int t = 0; t < 4; ++t) h[t] = pack_f16(ldexpf(bf16lo(w[t]), -e), ldexpf(bf16hi(w[t]), -e));
+  return e;
+}
+
 template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint16_t* __restrict__ k16,
-    int64_t n_bh, int Sq, int S_max, int pos0, int conv_first, const float2* __restrict__ table) {
+    uint8_t* __restrict__ kexp, int64_t n_bh, int Sq, int S_max, int pos0, int conv_first,
+    const float2* __restrict__ table) {
   constexpr int NCH = D / 8;  // 16-byte chunks per row
   // rows handled per (batch, KV head): [first, pos0 + Sq); with RoPE the earlier rows from
   // conv_first on (those a sliding window can still see) are converted to fp16
@@ -52,9 +69,9 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
       // earlier token (RoPE only): its stored bf16 key, converted to fp16
       const u32x4 w = *reinterpret_cast<const u32x4*>(k_cache + crow);
       u32x4 h;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) h[t] = pack_f16(bf16lo(w[t]), bf16hi(w[t]));
+      const int e = to_f16_row<NCH>(w, h);
       *reinterpret_cast<u32x4*>(k16 + (bh * Sk + s) * D + cc * 8) = h;
+      if (cc == 0) kexp[bh * Sk + s] = (uint8_t)e;
       continue;
     }
     const int64_t nrow = (bh * Sq + (s - pos0)) * D + cc * 8;  // element offset in the chunk
@@ -70,10 +87,11 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
         const float x0 = bf16lo(kw[p]), x1 = bf16hi(kw[p]);
         const float c = cs[2 * p], sn = cs[2 * p + 1];
         kb[p] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
-        kh[p] = pack_f16(bf16lo(kb[p]), bf16hi(kb[p]));
       }
+      const int e = to_f16_row<NCH>(kb, kh);
       *reinterpret_cast<u32x4*>(k_cache + crow) = kb;
       *reinterpret_cast<u32x4*>(k16 + (bh * Sk + s) * D + cc * 8) = kh;
+      if (cc == 0) kexp[bh * Sk + s] = (uint8_t)e;
     } else {
       *reinterpret_cast<u32x4*>(k_cache + crow) = kw;
     }
@@ -94,12 +112,13 @@ hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* 
   if (table)
     hipLaunchKernelGGL((cache_append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, (uint16_t*)k16, n_bh, Sq, S_max, pos0, conv_first,
-                       reinterpret_cast<const float2*>(table));
+                       (uint16_t*)v_cache, (uint16_t*)k16,
+                       static_cast<uint8_t*>(k16) + prefill_kexp_offset(B, Hkv, pos0 + Sq, D), n_bh, Sq,
+                       S_max, pos0, conv_first, reinterpret_cast<const float2*>(table));
   else
     hipLaunchKernelGGL((cache_append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
-                       (uint16_t*)v_cache, (uint16_t*)nullptr, n_bh, Sq, S_max, pos0, pos0,
+                       (uint16_t*)v_cache, (uint16_t*)nullptr, (uint8_t*)nullptr, n_bh, Sq, S_max, pos0, pos0,
                        (const float2*)nullptr);
   return hipGetLastError();
 }
@@ -108,8 +127,8 @@ template <int D, bool ROPE>
 __global__ __launch_bounds__(256) void cache_append_paged_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_pages,
     uint16_t* __restrict__ v_pages, const int32_t* __restrict__ block_table, int max_blocks, int bs_log2,
-    int num_blocks, uint16_t* __restrict__ k_ws, uint16_t* __restrict__ v_ws, int B, int Hkv, int Sq,
-    int pos0, int conv_first, int first_seen, const float2* __restrict__ table) {
+    int num_blocks, uint16_t* __restrict__ k_ws, uint8_t* __restrict__ kexp, uint16_t* __restrict__ v_ws, int B,
+    int Hkv, int Sq, int pos0, int conv_first, int first_seen, const float2* __restrict__ table) {
   constexpr int NCH = D / 8;  // 16-byte chunks per row
   const int Sk = pos0 + Sq;
   const int nrows = Sk - conv_first;
@@ -127,6 +146,7 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
       // read, so its block may have been released; zeros keep the masked products finite
       *reinterpret_cast<u32x4*>(k_ws + wrow) = u32x4{0, 0, 0, 0};
       *reinterpret_cast<u32x4*>(v_ws + wrow) = u32x4{0, 0, 0, 0};
+      if (ROPE && cc == 0) kexp[bh * Sk + s] = 0;
       continue;
     }
     int blk = block_table[(int64_t)b * max_blocks + (s >> bs_log2)];
@@ -137,8 +157,8 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
       const u32x4 w = *reinterpret_cast<const u32x4*>(k_pages + prow);
       u32x4 h = w;
       if constexpr (ROPE) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) h[t] = pack_f16(bf16lo(w[t]), bf16hi(w[t]));
+        const int e = to_f16_row<NCH>(w, h);
+        if (cc == 0) kexp[bh * Sk + s] = (uint8_t)e;
       }
       *reinterpret_cast<u32x4*>(k_ws + wrow) = h;
       *reinterpret_cast<u32x4*>(v_ws + wrow) = *reinterpret_cast<const u32x4*>(v_pages + prow);
@@ -157,8 +177,9 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
         const float x0 = bf16lo(kw[p]), x1 = bf16hi(kw[p]);
         const float c = cs[2 * p], sn = cs[2 * p + 1];
         kb[p] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
-        kh[p] = pack_f16(bf16lo(kb[p]), bf16hi(kb[p]));
       }
+      const int e = to_f16_row<NCH>(kb, kh);
+      if (cc == 0) kexp[bh * Sk + s] = (uint8_t)e;
       *reinterpret_cast<u32x4*>(k_pages + prow) = kb;
       *reinterpret_cast<u32x4*>(k_ws + wrow) = kh;
     } else {
@@ -182,8 +203,9 @@ hipError_t append_paged_go(const void* k_new, const void* v_new, void* k_pages, 
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)k_new,
                        (const uint16_t*)v_new, (uint16_t*)k_pages, (uint16_t*)v_pages, block_table, max_blocks,
-                       bs_log2, num_blocks, (uint16_t*)k_ws, (uint16_t*)v_ws, B, Hkv, Sq, pos0, conv_first,
-                       first_seen, reinterpret_cast<const float2*>(table));
+                       bs_log2, num_blocks, (uint16_t*)k_ws,
+                       static_cast<uint8_t*>(k_ws) + prefill_kexp_offset(B, Hkv, pos0 + Sq, D), (uint16_t*)v_ws,
+                       B, Hkv, Sq, pos0, conv_first, first_seen, reinterpret_cast<const float2*>(table));
     return hipGetLastError();
   };
   return table ? go(cache_append_paged_kernel<D, true>) : go(cache_append_paged_kernel<D, false>);

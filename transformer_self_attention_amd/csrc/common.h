@@ -52,6 +52,34 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // A value known to be the same in every lane, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ---- fp16 operands with a power-of-two row exponent ----
+// The Q.K^T products of the bf16 prefill take IEEE half operands (11 significant bits against
+// bf16's 8), whose range ends at 65504.  A row whose largest magnitude reaches 2^15 is stored
+// scaled by 2^-e, the smallest e >= 0 that brings it below 2^15 (so rounding to half cannot
+// overflow), and e is kept beside it; scaling by a power of two is exact, and rows with e = 0 are
+// stored exactly as before.  Non-finite rows keep e = 0.
+__device__ __forceinline__ int f16_row_exponent(float max_abs) {
+  const int eb = (int)((__float_as_uint(max_abs) >> 23) & 0xff);  // biased exponent
+  if (eb == 255) return 0;
+  const int u = eb - 127;  // max_abs in [2^u, 2^(u+1))
+  return u > 14 ? u - 14 : 0;
+}
+
+// Maximum of x over each aligned group of N consecutive lanes (N = 8 or 16), in every lane of
+// the group (DPP within rows of 16 lanes; all lanes of a group must be active).
+template <int N>
+__device__ __forceinline__ float group_max(float x) {
+  static_assert(N == 8 || N == 16, "group size");
+#define ATTN_DPP_MAX(v, ctrl) \
+  fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xf, 0xf, false)))
+  x = ATTN_DPP_MAX(x, 0xb1);   // quad_perm [1, 0, 3, 2]
+  x = ATTN_DPP_MAX(x, 0x4e);   // quad_perm [2, 3, 0, 1]
+  x = ATTN_DPP_MAX(x, 0x141);  // row_half_mirror: lanes i and 7 - i of each 8
+  if constexpr (N == 16) x = ATTN_DPP_MAX(x, 0x140);  // row_mirror: lanes i and 15 - i of each 16
+#undef ATTN_DPP_MAX
+  return x;
+}
+
 // ------------------------------------------------------------------------------------------
 // Launchers (each returns hipGetLastError() of its launch).  Arguments were validated by the
 // C-ABI layer; the launchers only size grids.
@@ -90,7 +118,10 @@ struct PrefillArgs {
   int window;
 };
 
+// Rotated keys as fp16 [B, Hkv, S, D], then one exponent byte per key row [B, Hkv, S] at byte
+// offset prefill_kexp_offset(...) (the rows' scale, see f16_row_exponent).
 size_t prefill_workspace_bytes(int B, int Hkv, int S, int D);
+inline size_t prefill_kexp_offset(int B, int Hkv, int S, int D) { return (size_t)B * Hkv * S * D * 2; }
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st);
 hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,

@@ -71,7 +71,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
                          const uint16_t* __restrict__ v, void* __restrict__ o,
                          float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Sk,
                          int k_rows, int v_rows, int coff, int window, int pos0,
-                         const float2* __restrict__ table) {
+                         const float2* __restrict__ table, const uint8_t* __restrict__ kexp) {
   constexpr int NT = NW * 64;                // threads per workgroup
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over D
@@ -91,6 +91,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   __shared__ __attribute__((aligned(16))) uint16_t k_lds1[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds0[TILE_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t v_lds1[TILE_ELEMS];
+  // fused mode, per stage: the exponent byte of each key row of the K tile (f16_row_exponent),
+  // and one byte per wave, set when some row it rotated has a non-zero exponent
+  __shared__ uint8_t e_lds[KMODE == KMODE_FUSED ? 2 : 1][KMODE == KMODE_FUSED ? kBN : 1];
+  __shared__ uint32_t e_flag[KMODE == KMODE_FUSED ? 2 : 1];
+  static_assert(KMODE != KMODE_FUSED || NW == 4, "one flag byte per wave, read as one word");
 
   // ---- workgroup -> (query block, batch, head) ----
   const int G = Hq / Hkv;
@@ -210,6 +215,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   };
   auto fused_store = [&](uint16_t* k_tile) {
     if constexpr (KMODE == KMODE_FUSED) {
+      bool wave_big = false;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + NT * i;
@@ -226,12 +232,26 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p] = x0 * c - x1 * s;
           x[2 * p + 1] = x0 * s + x1 * c;
         }
+        // The row's exponent: its NCH chunks are held by NCH consecutive lanes.  Rows below 2^15
+        // (every row, in practice) are packed as they are; only a wave holding a larger element
+        // finds the exponents of its rows.
+        const float mx = fmaxf(fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))),
+                               fmaxf(fmaxf(fabsf(x[4]), fabsf(x[5])), fmaxf(fabsf(x[6]), fabsf(x[7]))));
+        int e = 0;
+        if (__builtin_amdgcn_ballot_w64(!(mx < 32768.f)) != 0) {
+          e = f16_row_exponent(group_max<NCH>(mx));
+#pragma unroll
+          for (int t = 0; t < 8; ++t) x[t] = ldexpf(x[t], -e);
+          wave_big = true;
+        }
         u32x4 kh;
 #pragma unroll
         for (int t = 0; t < 4; ++t) kh[t] = pack_f16(x[2 * t], x[2 * t + 1]);
         const int off = r * D + swz<D>(r, cc) * 8;
         *reinterpret_cast<ATTN_LDS u32x4*>((ATTN_LDS uint16_t*)(k_tile) + off) = kh;
+        if (cc == 0) e_lds[k_tile == k_lds0 ? 0 : 1][r] = (uint8_t)e;
       }
+      if (lane == 0) reinterpret_cast<uint8_t*>(&e_flag[k_tile == k_lds0 ? 0 : 1])[wave] = wave_big ? 1 : 0;
     }
   };
   auto issue_tile = [&](int k0, uint16_t* k_tile, uint16_t* v_tile) {
@@ -255,11 +275,25 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   for (int r = 0; r < 16; ++r) s_init_v[r] = 0.f;
   typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // Row exponents of the fp16 operands (f16_row_exponent): qa of this lane's query row (q_scaled:
+  // some row of the wave has one), and the exponent byte of key row k0 + lane of the current tile
+  // (pre-rotated keys: loaded one tile ahead with the tile's loads).  A tile where any of them is
+  // non-zero forms its products from 0 and scales them, s - m = 2^(qa + e) q'.k' + s_init, which is
+  // as accurate as starting the products from s_init; other tiles take the usual path.
+  constexpr bool EXPS = !QK_BF16;
+  int qa = 0;
+  bool q_scaled = false;
+  int e_cur = 0, e_next = 0;
+  const uint8_t* kexp_head = kexp ? kexp + ((int64_t)b * Hkv + hkv) * k_rows : nullptr;
+  auto load_exps = [&](int k0) {
+    if constexpr (KMODE == KMODE_PREROT) e_next = kexp_head[min(k0 + lane, Sk - 1)];
+  };
 
   // One key tile: t is the tile index; the stage (and so every LDS address) is fixed at compile
   // time by STAGE.
-  auto tile_step = [&](auto stage_c, int t) {
+  auto tile_step = [&](auto stage_c, auto scaled_c, int t) {
     constexpr int STAGE = decltype(stage_c)::value;
+    constexpr bool SCALED = decltype(scaled_c)::value;
     uint16_t* k_cur = STAGE ? k_lds1 : k_lds0;
     uint16_t* v_cur = STAGE ? v_lds1 : v_lds0;
     uint16_t* k_nxt = STAGE ? k_lds0 : k_lds1;
@@ -270,28 +304,69 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     // makes every wave's part visible and guarantees every wave is done with tile t-1.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(k0 + kBN, k_nxt, v_nxt);
+    if constexpr (SCALED && KMODE == KMODE_PREROT) e_cur = e_next;
+    if (t + 1 < n_tiles) {
+      issue_tile(k0 + kBN, k_nxt, v_nxt);
+      if constexpr (SCALED) load_exps(k0 + kBN);
+    }
 
     if (!CAUSAL || (k0 <= qw + kRowsPerWave - 1 + coff && (!WIN || k0 + kBN - 1 >= qw + coff - window))) {
       const ATTN_LDS uint16_t* kb_lds = (const ATTN_LDS uint16_t*)(k_cur);
       const ATTN_LDS uint16_t* vb_lds = (const ATTN_LDS uint16_t*)(v_cur);
-      // S^T = K Q^T for two 32-key blocks
+      // S^T = K Q^T for two 32-key blocks, the products of each starting from c0
       f32x16 sacc[2];
+      auto scores = [&](const f32x16& c0) __attribute__((always_inline)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        qk_t a[KS];
+        for (int kb = 0; kb < 2; ++kb) {
+          qk_t a[KS];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>((const ATTN_LDS char*)kb_lds + kaddr[ks] + kb * 32 * D * 2);
+          for (int ks = 0; ks < KS; ++ks)
+            a[ks] = *reinterpret_cast<const ATTN_LDS qk_t*>((const ATTN_LDS char*)kb_lds + kaddr[ks] + kb * 32 * D * 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          // the first product starts from the offset block (s_init in every element)
-          const f32x16 c = ks == 0 ? s_init_v : sacc[kb];
-          if constexpr (QK_BF16)
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], c, 0, 0, 0);
-          else
-            sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], c, 0, 0, 0);
+          for (int ks = 0; ks < KS; ++ks) {
+            const f32x16 c = ks == 0 ? c0 : sacc[kb];
+            if constexpr (QK_BF16)
+              sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], qf[ks], c, 0, 0, 0);
+            else
+              sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[ks], qf[ks], c, 0, 0, 0);
+          }
         }
+      };
+      // key exponents of the tile: pre-rotated keys hold row k0 + lane's in e_cur; fused RoPE
+      // reads them from e_lds (the stage's bytes stay put until the next barrier)
+      auto key_exp = [&](int key) __attribute__((always_inline)) {
+        if constexpr (KMODE == KMODE_FUSED) return (int)e_lds[STAGE][key];
+        else return __builtin_amdgcn_ds_bpermute(key << 2, e_cur);
+      };
+      bool scaled_tile = false;
+      if constexpr (SCALED) {
+        if constexpr (KMODE == KMODE_FUSED)
+          scaled_tile = q_scaled || e_flag[STAGE] != 0;
+        else
+          scaled_tile = q_scaled || __builtin_amdgcn_ballot_w64(e_cur != 0) != 0;
+      }
+      // Scaled rows present (rare): the products start from 0 and become 2^(qa + e) q'.k' +
+      // s_init, with e the exponent of each score's key.  The offset block is cleared for the one
+      // score pass and restored afterwards, inside branches (the empty asm keeps the compiler from
+      // turning them into a select of every element on every tile).
+      if (scaled_tile) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_init_v[r] = 0.f;
+        asm volatile("");
+      }
+      // the first product starts from the offset block (s_init in every element)
+      scores(s_init_v);
+      if (scaled_tile) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int ek = key_exp(kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3));
+            sacc[kb][r] = ldexpf(sacc[kb][r], qa + ek) + s_init;
+          }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s_init_v[r] = s_init;
+        asm volatile("");
       }
       if constexpr (QK_BF16) {
 #pragma unroll
@@ -439,6 +514,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // overlap at the start of every workgroup.
   issue_tile(t_first * kBN, k_lds0, v_lds0);
   fused_issue(t_first * kBN);
+  load_exps(t_first * kBN);
   {
     const int rc = row < Sq ? row : Sq - 1;
     const uint16_t* qrow = q + (((int64_t)b * Hq + h) * Sq + rc) * D;
@@ -446,10 +522,14 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * hl;
       const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
-      if constexpr (QK_BF16) {
-        qf[ks] = __builtin_bit_cast(bf16x8, w);
-      } else {
-        float x[8];
+      if constexpr (QK_BF16) qf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+    if constexpr (!QK_BF16) {
+      // the row rotated and scaled by log2(e)/sqrt(D): once for the row's exponent, once more to
+      // round it (scaled by 2^-qa) to fp16
+      auto rotated = [&](int ks, float (&x)[8]) __attribute__((always_inline)) {
+        const int d0 = 16 * ks + 8 * hl;
+        const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
 #pragma unroll
         for (int t = 0; t < 4; ++t) { x[2 * t] = bf16lo(w[t]); x[2 * t + 1] = bf16hi(w[t]); }
         const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + rc) * (D / 2) + d0 / 2);
@@ -459,18 +539,61 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         for (int p = 0; p < 4; ++p) {
           const float c = cs[2 * p], s = cs[2 * p + 1];
           const float x0 = x[2 * p], x1 = x[2 * p + 1];
-          x[2 * p] = x0 * c - x1 * s;
-          x[2 * p + 1] = x0 * s + x1 * c;
+          x[2 * p] = (x0 * c - x1 * s) * c_log2;
+          x[2 * p + 1] = (x0 * s + x1 * c) * c_log2;
         }
+      };
+      float qmax = 0.f;
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)(x[t] * c_log2);
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        rotated(ks, x);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qmax = fmaxf(qmax, fabsf(x[t]));
+      }
+      qa = f16_row_exponent(fmaxf(qmax, swap_halves(qmax)));
+      q_scaled = __builtin_amdgcn_ballot_w64(qa != 0) != 0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+        rotated(ks, x);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)ldexpf(x[t], -qa);
       }
     }
   }
 
-  for (int t = t_first; t < n_tiles; t += 2) {
-    tile_step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, t + 1);
+  // Which key loop: the scaled one tests every tile for row exponents; the plain one has no such
+  // test.  Fused RoPE finds the key exponents only tile by tile, so it always takes the scaled
+  // loop; bf16 operands (no RoPE) have none.  Pre-rotated keys: every thread ORs 16-byte words of
+  // the exponent bytes covering [t_first * kBN, key_end), and the workgroup takes the scaled loop
+  // if any exponent there, or any qa of its rows, is non-zero.  The exponent area starts 16-byte
+  // aligned and its size is rounded up to 256 bytes, so the words stay inside it; bytes of
+  // neighbouring rows only make the test conservative.
+  bool scaled_wg = KMODE == KMODE_FUSED;
+  if constexpr (KMODE == KMODE_PREROT) {
+    uint32_t acc = q_scaled ? 1u : 0u;
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(kexp_head + t_first * kBN) & ~(uintptr_t)15;
+    const uintptr_t hi = (reinterpret_cast<uintptr_t>(kexp_head + key_end) + 15) & ~(uintptr_t)15;
+    for (uintptr_t p = lo + 16 * (uintptr_t)tid; p < hi; p += 16 * NT) {
+      const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+      acc |= w[0] | w[1] | w[2] | w[3];
+    }
+    scaled_wg = __syncthreads_or(acc != 0) != 0;
+  }
+  auto key_loop = [&](auto scaled_c) __attribute__((always_inline)) {
+    for (int t = t_first; t < n_tiles; t += 2) {
+      tile_step(std::integral_constant<int, 0>{}, scaled_c, t);
+      if (t + 1 < n_tiles) tile_step(std::integral_constant<int, 1>{}, scaled_c, t + 1);
+    }
+  };
+  if constexpr (EXPS) {
+    if (scaled_wg)
+      key_loop(std::true_type{});
+    else
+      key_loop(std::false_type{});
+  } else {
+    key_loop(std::false_type{});
   }
 
   // ---- finalize ----
@@ -506,10 +629,14 @@ hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   const int nqb = (a.S + BM - 1) / BM;
   const int64_t NG = (int64_t)nqb * a.B * a.Hkv;
   const int64_t blocks = ((NG + kNumXcd - 1) / kNumXcd) * kNumXcd * G;
+  // pre-rotated keys: their exponent bytes follow the fp16 rows (k_rows per batch and KV head)
+  const uint8_t* kexp = KMODE == KMODE_PREROT
+                            ? static_cast<const uint8_t*>(kptr) + prefill_kexp_offset(a.B, a.Hkv, a.k_rows, D)
+                            : nullptr;
   hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW, WIN>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.Sk, a.k_rows,
-                     a.v_rows, a.coff, a.window, a.pos0, reinterpret_cast<const float2*>(a.table));
+                     a.v_rows, a.coff, a.window, a.pos0, reinterpret_cast<const float2*>(a.table), kexp);
   return hipGetLastError();
 }
 
@@ -536,7 +663,8 @@ hipError_t dispatch_d(const PrefillArgs& a, hipStream_t st) {
 }  // namespace
 
 size_t prefill_workspace_bytes(int B, int Hkv, int S, int D) {
-  return (size_t)B * Hkv * S * D * 2;
+  const size_t exps = ((size_t)B * Hkv * S + 255) / 256 * 256;
+  return prefill_kexp_offset(B, Hkv, S, D) + exps;
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {

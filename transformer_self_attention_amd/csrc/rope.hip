@@ -200,15 +200,18 @@ hipError_t launch_rope_apply(const void* x, void* out, bool bf16, int64_t rows, 
 
 
 // One pass over K: rotate every row at position pos0 + s (fp32 arithmetic, the same coefficient
-// table) and store it as fp16, the operand format of the Q.K^T product of the bf16 prefill.  K is
-// not read again, so its loads are nontemporal and leave the caches to the fp16 copy and V (a
-// whole MHA step at 2k tokens +1 to +5%).
+// table) and store it as fp16, the operand format of the Q.K^T product of the bf16 prefill, with
+// the row's power-of-two exponent (f16_row_exponent: rows reaching 2^15 are stored scaled down,
+// their exponent byte in kexp [bh_count, S]).  K is not read again, so its loads are nontemporal
+// and leave the caches to the fp16 copy and V (a whole MHA step at 2k tokens +1 to +5%).
 template <int D, int HPT>
 __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restrict__ k,
-                                                         uint16_t* __restrict__ out, int64_t bh_count, int S,
-                                                         int pos0, const float2* __restrict__ table) {
+                                                         uint16_t* __restrict__ out, uint8_t* __restrict__ kexp,
+                                                         int64_t bh_count, int S, int pos0,
+                                                         const float2* __restrict__ table) {
   // Each lane rotates 4 pairs at one position in HPT consecutive (batch, head) row blocks: one
   // load of its table entries serves all of them, and a full group's loads issue back to back.
+  // The NCH lanes of one row are consecutive (aligned), so a row's maximum is a group reduction.
   constexpr int NCH = D / 8;
   const int64_t n_groups = (bh_count + HPT - 1) / HPT;
   const int64_t per_group = (int64_t)S * NCH;
@@ -226,15 +229,24 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
     const int64_t bh0 = group * HPT;
     const int64_t base = (bh0 * S + s) * D + cc * 8;
     const int nh = bh_count - bh0 < HPT ? (int)(bh_count - bh0) : HPT;
-    auto rotate = [&](const u32x4 w) {
-      u32x4 hw;
+    // rotate, then scale the row by its exponent and store it as fp16
+    auto rotate_store = [&](const u32x4 w, int hh) {
+      float r[8];
+      float mx = 0.f;
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         const float x0 = bf16lo(w[p]), x1 = bf16hi(w[p]);
         const float c = cs[2 * p], sn = cs[2 * p + 1];
-        hw[p] = pack_f16(fmaf(x0, c, -(x1 * sn)), fmaf(x1, c, x0 * sn));
+        r[2 * p] = fmaf(x0, c, -(x1 * sn));
+        r[2 * p + 1] = fmaf(x1, c, x0 * sn);
+        mx = fmaxf(mx, fmaxf(fabsf(r[2 * p]), fabsf(r[2 * p + 1])));
       }
-      return hw;
+      const int e = f16_row_exponent(group_max<NCH>(mx));
+      u32x4 hw;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) hw[p] = pack_f16(ldexpf(r[2 * p], -e), ldexpf(r[2 * p + 1], -e));
+      *reinterpret_cast<u32x4*>(out + base + hh * bh_stride) = hw;
+      if (cc == 0) kexp[(bh0 + hh) * S + s] = (uint8_t)e;
     };
     if (nh == HPT) {
       u32x4 w[HPT];
@@ -242,12 +254,10 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
       for (int h = 0; h < HPT; ++h)
         w[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + base + h * bh_stride));
 #pragma unroll
-      for (int h = 0; h < HPT; ++h) *reinterpret_cast<u32x4*>(out + base + h * bh_stride) = rotate(w[h]);
+      for (int h = 0; h < HPT; ++h) rotate_store(w[h], h);
     } else {
-      for (int h = 0; h < nh; ++h) {
-        const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + base + h * bh_stride));
-        *reinterpret_cast<u32x4*>(out + base + h * bh_stride) = rotate(w);
-      }
+      for (int h = 0; h < nh; ++h)
+        rotate_store(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k + base + h * bh_stride)), h);
     }
   }
 }
@@ -259,8 +269,9 @@ static hipError_t rotate_keys(const void* k, void* k_rot, int64_t rows, int S, i
   const int64_t bh_count = rows / S;
   int64_t blocks = ((bh_count + HPT - 1) / HPT * S * (D / 8) + 255) / 256;
   if (blocks > 16384) blocks = 16384;
+  uint8_t* kexp = static_cast<uint8_t*>(k_rot) + rows * D * 2;
   hipLaunchKernelGGL((rope_k_f16_kernel<D, HPT>), dim3((unsigned)blocks), dim3(256), 0, st,
-                     (const uint16_t*)k, (uint16_t*)k_rot, bh_count, S, pos0,
+                     (const uint16_t*)k, (uint16_t*)k_rot, kexp, bh_count, S, pos0,
                      reinterpret_cast<const float2*>(table));
   return hipGetLastError();
 }

@@ -306,7 +306,9 @@ def prefill(q, k, v, table=None, *, causal=True, pos0=0, window=None, out=None, 
 
 
 def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
-    """Rotated keys as fp16 (a torch.float16 tensor shaped like k), for prefill_prerotated."""
+    """Rotated keys for prefill_prerotated: a uint8 GPU buffer of prefill_workspace_bytes(B, Hkv, S, D)
+    bytes holding the rotated rows as fp16 [B, Hkv, S, D] (rows reaching 2^15 scaled by a power of
+    two), then one exponent byte per row.  rotated_keys_view() shows the fp16 part."""
     _need(k, "k")
     if k.dim() != 4:
         raise ValueError("k must be [B, Hkv, S, D]")
@@ -316,18 +318,40 @@ def rotate_keys_f16(k, table, pos0=0, out=None, stream=None):
     tmax = _table(table, D, k.device)
     if tmax == 0:
         raise ValueError("rotate_keys_f16 needs a table")
-    out = _out(out, k.shape, torch.float16, k.device)
+    need = prefill_workspace_bytes(B, Hkv, S, D)
+    if out is None:
+        out = torch.empty(need, dtype=torch.uint8, device=k.device)
+    _need(out, "out", k.device)
+    if out.dtype != torch.uint8 or out.numel() < need:
+        raise ValueError(f"out must be a uint8 buffer of at least {need} bytes")
     _check(_lib.attn_rotate_keys_f16(_ptr(k), _ptr(out), B, Hkv, S, D, pos0, _ptr(table), tmax,
                                      _stream(stream)), "attn_rotate_keys_f16")
     return out
 
 
+def rotated_keys_view(buf, B, Hkv, S, D):
+    """The fp16 rows [B, Hkv, S, D] of a rotate_keys_f16 buffer, and its exponent bytes [B, Hkv, S]."""
+    n = B * Hkv * S * D * 2
+    return buf[:n].view(torch.float16).view(B, Hkv, S, D), buf[n:n + B * Hkv * S].view(B, Hkv, S)
+
+
 def prefill_prerotated(q, k_rot, v, table, *, causal=True, pos0=0, window=None, out=None, out_dtype=None,
                        lse=None, stream=None):
-    """prefill() for keys already rotated by rotate_keys_f16 (same table and pos0)."""
-    B, Hq, Hkv, S, D = _qkv(q, k_rot, v)
-    if k_rot.dtype != torch.float16 or q.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
-        raise TypeError("q, v bfloat16 and k_rot float16 expected")
+    """prefill() for keys already rotated by rotate_keys_f16 (same table and pos0); k_rot is its
+    uint8 buffer, v gives B, Hkv, S and D."""
+    _need(q, "q")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q and v must be [B, H, S, D]")
+    B, Hq, S, D = q.shape
+    Hkv = v.shape[1]
+    _need(v, "v", q.device)
+    _shape(v, (B, Hkv, S, D), "v")
+    _need(k_rot, "k_rot", q.device)
+    need = prefill_workspace_bytes(B, Hkv, S, D)
+    if k_rot.dtype != torch.uint8 or k_rot.numel() < need:
+        raise ValueError(f"k_rot must be the uint8 buffer of rotate_keys_f16 ({need} bytes)")
+    if q.dtype != torch.bfloat16 or v.dtype != torch.bfloat16:
+        raise TypeError("q and v must be bfloat16")
     tmax = _table(table, D, q.device)
     if tmax == 0:
         raise ValueError("prefill_prerotated needs a table")
