@@ -59,17 +59,23 @@ typedef enum {
   ATTN_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
 } attn_status;
 
+/* The enumerations taken as arguments span every int (their _RANGE_ members), so that any int
+ * a caller passes is a value of the type; those outside the named ones are rejected with
+ * ATTN_ERR_INVALID_ARG. */
 typedef enum {
   ATTN_F32 = 0,  /* IEEE binary32 */
-  ATTN_BF16 = 1  /* bfloat16; results are rounded to nearest, ties to even */
+  ATTN_BF16 = 1, /* bfloat16; results are rounded to nearest, ties to even */
+  ATTN_DTYPE_RANGE_MIN_ = -2147483647 - 1,
+  ATTN_DTYPE_RANGE_MAX_ = 2147483647
 } attn_dtype;
 
 /* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
  * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys. */
 int attn_version(void);
 
-/* Human-readable name of a status code (static string, never NULL). */
-const char* attn_status_string(attn_status s);
+/* Human-readable name of a status code (static string, never NULL).  Any int is accepted; a value
+ * that is no attn_status gives "unknown attn_status". */
+const char* attn_status_string(int status);
 
 /* ---------------------------------------------------------------------------------------
  * RoPE coefficient table.
@@ -104,7 +110,14 @@ attn_status attn_rope_table_init(float* table, int max_pos, int D, double base, 
  * factor < 1 or not finite, NTK with D < 4, YaRN with original_max_pos < 1 or
  * beta_fast <= beta_slow.
  * --------------------------------------------------------------------------------------- */
-typedef enum { ATTN_ROPE_PLAIN = 0, ATTN_ROPE_PI = 1, ATTN_ROPE_NTK = 2, ATTN_ROPE_YARN = 3 } attn_rope_scaling;
+typedef enum {
+  ATTN_ROPE_PLAIN = 0,
+  ATTN_ROPE_PI = 1,
+  ATTN_ROPE_NTK = 2,
+  ATTN_ROPE_YARN = 3,
+  ATTN_ROPE_RANGE_MIN_ = -2147483647 - 1,
+  ATTN_ROPE_RANGE_MAX_ = 2147483647
+} attn_rope_scaling;
 attn_status attn_rope_table_init_scaled(float* table, int max_pos, int D, double base,
                                         attn_rope_scaling scaling, double factor, int original_max_pos,
                                         double beta_fast, double beta_slow, void* stream);

@@ -72,6 +72,53 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+# Host code of the C ABI (argument validation, dispatch) under AddressSanitizer and UBSan; device
+# code is built as usual.  Each sanitizer flag applies to the host pass only.
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def asan_runtime() -> str:
+    """The shared ASan runtime of the ROCm clang; a process that loads the host-sanitized library
+    must preload it (LD_PRELOAD)."""
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    clang = os.path.join(rocm, "lib", "llvm", "lib", "clang")
+    for ver in sorted(os.listdir(clang)) if os.path.isdir(clang) else []:
+        path = os.path.join(clang, ver, "lib", "linux", "libclang_rt.asan-x86_64.so")
+        if os.path.exists(path):
+            return path
+    raise RuntimeError(f"no libclang_rt.asan-x86_64.so under {clang}")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libattn.so with the host code of attn_api.hip under ASan + UBSan (-O1 -g), at
+    _build/sanitize/libattn_sanitized.so; load it with ATTN_LIBRARY=<path> and the runtime of
+    asan_runtime() preloaded."""
+    out_dir = os.path.join(BUILD_DIR, "sanitize")
+    os.makedirs(out_dir, exist_ok=True)
+
+    def one(src):
+        obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+        flags = list(COMMON_FLAGS)
+        if os.path.basename(src) == "attn_api.hip":
+            flags = [f for f in flags if f != "-O3"] + ["-O1", "-g", *SANITIZE_HOST]
+        res = subprocess.run([hipcc(), *flags, "-c", src, "-o", obj], capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n{res.stdout}{res.stderr}")
+        return obj
+
+    srcs = sources()
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(one, srcs))
+    path = os.path.join(out_dir, "libattn_sanitized.so")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-shared-libasan", *SANITIZE_HOST[:4],
+           "-o", path, *objs]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
+    return path
+
+
 if __name__ == "__main__":
     path = build(verbose="--verbose" in sys.argv)
     print(path)

@@ -149,8 +149,8 @@ extern "C" {
 
 int attn_version(void) { return kVersion; }
 
-const char* attn_status_string(attn_status s) {
-  switch (s) {
+const char* attn_status_string(int status) {
+  switch (status) {
     case ATTN_OK: return "ATTN_OK";
     case ATTN_ERR_INVALID_ARG: return "ATTN_ERR_INVALID_ARG: invalid argument";
     case ATTN_ERR_UNSUPPORTED: return "ATTN_ERR_UNSUPPORTED: outside the support matrix";

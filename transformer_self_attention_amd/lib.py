@@ -14,7 +14,9 @@ import os
 
 import torch  # loads torch's HIP runtime first, so libattn.so binds to the same one
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
+# ATTN_LIBRARY: another build of the same library to load instead (the host-sanitized build of
+# build.build_host_sanitized(), for instance)
+_LIB_PATH = os.environ.get("ATTN_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libattn.so")
 
 ATTN_OK, ATTN_ERR_INVALID_ARG, ATTN_ERR_UNSUPPORTED, ATTN_ERR_HIP = 0, 1, 2, 3
 ATTN_F32, ATTN_BF16 = 0, 1
