@@ -70,8 +70,20 @@ typedef enum {
 } attn_dtype;
 
 /* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
- * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys. */
+ * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys; 2.1.0:
+ * attn_checked_sites. */
 int attn_version(void);
+
+/* Index checks of a checked build (the library compiled with ATTN_CHECKED; a debugging aid, not
+ * the product build).  There every kernel tests the largest index each thread is about to use
+ * against the extents its arguments give; a failed test sets a bit in a per-source-file word
+ * and the thread skips the accesses it guards instead of faulting.  This call copies up to n of
+ * those words into words (when not NULL), in the order rope, cache, prefill_bf16, prefill_f32,
+ * decode, decode_wide (bit i of a word: check site i of that file, named in its source), clears
+ * them, and returns the number of words (6).  The copies are blocking: call it once the work
+ * checked has completed, with no other call on the device in flight.  A normal build returns -1
+ * and touches nothing. */
+int attn_checked_sites(unsigned int* words, int n);
 
 /* Human-readable name of a status code (static string, never NULL).  Any int is accepted; a value
  * that is no attn_status gives "unknown attn_status". */

@@ -10,6 +10,27 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
 
+# With ATTN_CHECKED_RUN=1 (tests/test_gpu_checked.py sets it, with ATTN_LIBRARY pointing at the
+# index-checked build), every GPU test ends by reading the words of failed index checks: any set
+# bit fails the test.
+import pytest  # noqa: E402
+
+
+@pytest.fixture(autouse=True)
+def _checked_build_sites(request):
+    yield
+    if os.environ.get("ATTN_CHECKED_RUN") != "1" or request.node.get_closest_marker("gpu") is None:
+        return
+    import torch
+    from transformer_self_attention_amd import lib
+    torch.cuda.synchronize()
+    words = lib.checked_sites()
+    assert words is not None, "ATTN_CHECKED_RUN=1 but the loaded library is not the checked build"
+    files = ("rope", "cache", "prefill_bf16", "prefill_f32", "decode", "decode_wide")
+    failed = {f: [i for i in range(32) if w >> i & 1] for f, w in zip(files, words) if w}
+    assert not failed, f"failed index checks (file: sites): {failed}"
+
+
 # ---- helpers shared by the GPU tests -------------------------------------------------------
 import numpy as np  # noqa: E402
 

@@ -35,7 +35,8 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lib.version() == 20000
+    assert lib.version() == 20100
+    assert lib.checked_sites() is None     # the normal build has no index checks
     assert lib.status_string(OK) == "ATTN_OK"
     for s in (INV, UNSUP, lib.ATTN_ERR_HIP):
         assert lib.status_string(s).startswith("ATTN_ERR_")

@@ -1,0 +1,53 @@
+"""GPU tests against the index-checked build (libattn_checked.so, build.build_checked()).
+
+A child process runs a selection of the GPU parity, canary and edge tests with ATTN_LIBRARY
+pointing at the checked build and ATTN_CHECKED_RUN=1, so that each of those tests also asserts
+that no kernel index check failed (tests/conftest.py reads the check words after each one).  The
+selection covers every kernel: RoPE apply and key rotation, prefill in the three key modes and in
+fp32, decode (narrow and wide kernels, with and without the merge pass, paged, windowed), the
+contiguous and paged chunk appends, and the fp16-range paths."""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+SELECTION = [
+    "tests/test_gpu_parity.py::test_rope_apply_random",
+    "tests/test_gpu_parity.py::test_prefill_tiny_fp32_config",
+    "tests/test_gpu_parity.py::test_prefill_fp32_ragged",
+    "tests/test_gpu_parity.py::test_prefill_bf16_ragged",
+    "tests/test_gpu_parity.py::test_two_stage_prefill_equals_one_call",
+    "tests/test_gpu_parity.py::test_decode_edges",
+    "tests/test_gpu_chunk.py::test_chunk_against_oracle",
+    "tests/test_gpu_chunk_paged.py::test_paged_chunk_against_contiguous_and_oracle",
+    "tests/test_gpu_decode_wide.py::test_decode_wide_groups",
+    "tests/test_gpu_decode_wide.py::test_decode_wide_paged",
+    "tests/test_gpu_window.py::test_prefill_window",
+    "tests/test_gpu_window.py::test_prefill_window_fp32",
+    "tests/test_gpu_window.py::test_chunk_window",
+    "tests/test_gpu_window.py::test_decode_window",
+    "tests/test_gpu_window.py::test_paged_decode_window_skips_released_blocks",
+    "tests/test_gpu_canaries.py",
+    "tests/test_gpu_fp16_range.py::test_prefill_large_rows",
+]
+
+
+@pytest.mark.timeout(600)
+def test_gpu_tests_pass_on_the_checked_build():
+    from transformer_self_attention_amd import build
+    lib = build.CHECKED_LIB_PATH
+    assert os.path.exists(lib), f"{lib} is missing: __graft_entry__.build() makes it"
+    env = dict(os.environ, ATTN_LIBRARY=lib, ATTN_CHECKED_RUN="1")
+    print(f"\n[case] checked build: {len(SELECTION)} test groups in a child process", flush=True)
+    res = subprocess.run([sys.executable, "-u", "-m", "pytest", "-q", "-x", "-m", "gpu", "-p", "no:cacheprovider",
+                          *SELECTION], cwd=ROOT, env=env, capture_output=True, text=True, timeout=560)
+    tail = res.stdout[-6000:] + res.stderr[-2000:]
+    print(tail, flush=True)
+    assert res.returncode == 0, tail
+    assert " passed" in res.stdout and " failed" not in res.stdout

@@ -45,9 +45,9 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, verbose: bool, obj_dir: str = BUILD_DIR, extra=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops"  # host pass does not know the device-only feature flag
     msgs = "\n".join(line for line in (res.stdout + res.stderr).splitlines() if noise not in line)
@@ -58,18 +58,33 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def _build(out: str, obj_dir: str, extra=(), verbose: bool = False) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sources()
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB_PATH + ".tmp"
+        objs = list(ex.map(lambda s: _compile(s, verbose, obj_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}{res.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """libattn.so, the product build."""
+    return _build(LIB_PATH, BUILD_DIR, verbose=verbose)
+
+
+CHECKED_LIB_PATH = os.path.join(PKG_DIR, "libattn_checked.so")
+
+
+def build_checked(verbose: bool = False) -> str:
+    """libattn_checked.so: the same sources with ATTN_CHECKED defined, so every kernel tests its
+    indices before the accesses they guard and reports failures through attn_checked_sites()
+    (load it with ATTN_LIBRARY=<path>).  A debugging aid, never the product path."""
+    return _build(CHECKED_LIB_PATH, os.path.join(BUILD_DIR, "checked"), extra=("-DATTN_CHECKED",), verbose=verbose)
 
 
 # Host code of the C ABI (argument validation, dispatch) under AddressSanitizer and UBSan; device

@@ -12,7 +12,8 @@
 
 namespace {
 
-constexpr int kVersion = 20000;  // 2.0.0
+constexpr int kVersion = 20100;  // 2.1.0
+constexpr int kCheckedWords = 6;  // source files with index checks (attn_checked_sites)
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -148,6 +149,20 @@ void* scratch_on_current_device() {
 extern "C" {
 
 int attn_version(void) { return kVersion; }
+
+int attn_checked_sites(unsigned int* words, int n) {
+#ifdef ATTN_CHECKED
+  const unsigned int w[kCheckedWords] = {attn::checked_word_rope(),         attn::checked_word_cache(),
+                                         attn::checked_word_prefill_bf16(), attn::checked_word_prefill_f32(),
+                                         attn::checked_word_decode(),       attn::checked_word_decode_wide()};
+  for (int i = 0; words && i < n && i < kCheckedWords; ++i) words[i] = w[i];
+  return kCheckedWords;
+#else
+  (void)words;
+  (void)n;
+  return -1;
+#endif
+}
 
 const char* attn_status_string(int status) {
   switch (status) {

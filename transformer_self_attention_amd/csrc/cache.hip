@@ -65,6 +65,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     const int s = first + (int)(rr % nrows);
     const int64_t bh = rr / nrows;
     const int64_t crow = (bh * S_max + s) * D + cc * 8;  // element offset in the cache
+    // checked build, site 0: the row in the cache, in the fp16 copy and in the chunk
+    if (!ATTN_IN(bh < n_bh && s >= 0 && s < Sk && Sk <= S_max && (s < pos0 || s - pos0 < Sq), 0)) continue;
     if (s < pos0) {
       // earlier token (RoPE only): its stored bf16 key, converted to fp16
       const u32x4 w = *reinterpret_cast<const u32x4*>(k_cache + crow);
@@ -141,6 +143,8 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
     const int64_t bh = rr / nrows;
     const int b = (int)(bh / Hkv), hkv = (int)(bh % Hkv);
     const int64_t wrow = (bh * Sk + s) * D + cc * 8;  // element offset in the workspace copies
+    // checked build, site 1: the row in the workspace copies, and its table entry
+    if (!ATTN_IN(b < B && s >= 0 && s < Sk && (s >> bs_log2) < max_blocks, 1)) continue;
     if (s < first_seen) {
       // before every query's window (in the first tile the attention reads, masked there): never
       // read, so its block may have been released; zeros keep the masked products finite
@@ -152,6 +156,8 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
     int blk = block_table[(int64_t)b * max_blocks + (s >> bs_log2)];
     blk = min(max(blk, 0), num_blocks - 1);
     const int64_t prow = ((((int64_t)blk * Hkv + hkv) << bs_log2) + (s & ((1 << bs_log2) - 1))) * D + cc * 8;
+    // checked build, site 2: the slot in the pool
+    if (!ATTN_IN(prow + 8 <= ((int64_t)num_blocks * Hkv << bs_log2) * D, 2)) continue;
     if (s < pos0) {
       // earlier token: its stored key (to fp16 with RoPE) and value, gathered
       const u32x4 w = *reinterpret_cast<const u32x4*>(k_pages + prow);
@@ -212,6 +218,8 @@ hipError_t append_paged_go(const void* k_new, const void* v_new, void* k_pages, 
 }
 
 }  // namespace
+
+ATTN_CHECK_READER(checked_word_cache)
 
 hipError_t launch_cache_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                                      const int32_t* block_table, int max_blocks, int bs_log2, int num_blocks,

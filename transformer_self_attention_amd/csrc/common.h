@@ -52,6 +52,46 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // A value known to be the same in every lane, moved to a scalar register.
 __device__ __forceinline__ int wave_uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ---- the checked build ----
+// Built with ATTN_CHECKED defined, the kernels test the largest index each thread is about to use
+// against the extents their own arguments give, at the point where that thread's index set is
+// fixed.  A failed test sets bit `site` of this source file's check word and the thread skips the
+// accesses it guards, so a bad index shows as a reported site instead of a memory fault; the
+// words are read and cleared through attn_checked_sites().  Every test holds for a whole row (or
+// a whole wave), so the lanes that share a row reduction stay together.  In the normal build
+// ATTN_IN(cond, site) is the constant true and the tests compile away.
+#ifdef ATTN_CHECKED
+namespace {
+__device__ unsigned int g_check_word;  // one per source file
+}
+__device__ __forceinline__ bool checked_in(bool ok, int site) {
+  if (!ok) atomicOr(&g_check_word, 1u << site);
+  return ok;
+}
+#define ATTN_IN(cond, site) (::attn::checked_in((cond), (site)))
+// Host reader of this source file's word (read, then cleared), named `fn`.
+#define ATTN_CHECK_READER(fn)                                                                      \
+  unsigned int fn() {                                                                              \
+    unsigned int w = 0, zero = 0;                                                                  \
+    if (hipMemcpyFromSymbol(&w, HIP_SYMBOL(g_check_word), sizeof(w), 0, hipMemcpyDeviceToHost) != \
+        hipSuccess)                                                                                \
+      return ~0u;                                                                                  \
+    if (hipMemcpyToSymbol(HIP_SYMBOL(g_check_word), &zero, sizeof(zero), 0, hipMemcpyHostToDevice) != \
+        hipSuccess)                                                                                \
+      return ~0u;                                                                                  \
+    return w;                                                                                      \
+  }
+unsigned int checked_word_rope();
+unsigned int checked_word_cache();
+unsigned int checked_word_prefill_bf16();
+unsigned int checked_word_prefill_f32();
+unsigned int checked_word_decode();
+unsigned int checked_word_decode_wide();
+#else
+#define ATTN_IN(cond, site) true
+#define ATTN_CHECK_READER(fn)
+#endif
+
 // ---- fp16 operands with a power-of-two row exponent ----
 // The Q.K^T products of the bf16 prefill take IEEE half operands (11 significant bits against
 // bf16's 8), whose range ends at 65504.  A row whose largest magnitude reaches 2^15 is stored

@@ -138,6 +138,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // nothing visible in this split: empty range (then every sub-block processed below holds at
   // least one visible row, the first one holding wstart)
   const int kend = wstart < kend0 ? kend0 : 0;
+  // checked build, site 0: the workgroup's (sequence, KV head, split, query heads) and key range
+  if (!ATTN_IN(b < B && hkv < Hkv && split < n_split && h0 >= 0 && h0 + max(Gs, 1) <= Hq && kbeg >= 0 &&
+                   kend <= S_max,
+               0))
+    return;
 
   // ---- query fragments (hi/lo bf16), rotated at q_pos[b] and scaled by log2(e)/sqrt(D) ----
   bf16x8 qhi[KS], qlo[KS];
@@ -190,10 +195,11 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // end of the cache reuses the first half's block, so every address stays inside a block).
   auto half_rows = [&](int k0, int64_t& r0, int64_t& r1) {
     const int k0u = wave_uniform(k0);
-    int blk0 = wave_uniform(btr[k0u >> bs_log2]);
+    // checked build, site 2: the block table entries read lie in this sequence's row of the table
+    int blk0 = wave_uniform(btr[ATTN_IN((k0u >> bs_log2) < max_blocks, 2) ? k0u >> bs_log2 : 0]);
     int blk1 = blk0;
     const int k1 = k0u + 16;
-    if (k1 < kend) blk1 = wave_uniform(btr[k1 >> bs_log2]);
+    if (k1 < kend) blk1 = wave_uniform(btr[ATTN_IN((k1 >> bs_log2) < max_blocks, 2) ? k1 >> bs_log2 : 0]);
     blk0 = min(max(blk0, 0), num_blocks - 1);
     blk1 = min(max(blk1, 0), num_blocks - 1);
     r0 = (((int64_t)blk0 * Hkv + hkv) << bs_log2) + (k0u & bmask);
@@ -217,6 +223,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       int64_t row;
       if constexpr (PAGED) row = ok ? (kb ? r1 : r0) + i16 : r0;
       else row = ok ? key : kbeg;
+      // checked build, site 1: the key row inside the cache (or the pool)
+      row = ATTN_IN(row >= 0 && row < (PAGED ? ((int64_t)num_blocks * Hkv << bs_log2) : (int64_t)S_max), 1) ? row : 0;
       const uint16_t* kp = kg + row * D + 8 * g16;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -232,6 +240,8 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
       int64_t row;
       if constexpr (PAGED) row = ok ? ((c / NCH) >= 16 ? r1 : r0) + ((c / NCH) & 15) : r0;
       else row = ok ? key : kbeg;
+      // checked build, site 1: the value row inside the cache (or the pool)
+      row = ATTN_IN(row >= 0 && row < (PAGED ? ((int64_t)num_blocks * Hkv << bs_log2) : (int64_t)S_max), 1) ? row : 0;
       const u32x4* src = reinterpret_cast<const u32x4*>(vg + row * D + (c % NCH) * 8);
       vst[i] = STREAM ? __builtin_nontemporal_load(src) : *src;
       if (!ok) vst[i] = u32x4{0, 0, 0, 0};
@@ -346,6 +356,7 @@ __global__ __launch_bounds__(NW * 64) void decode_split_kernel(
   // thread -> (row, d) pairs of the merged partial
   for (int e = tid; e < Gs * D; e += kThreads) {
     const int rr = e / D, d = e % D;
+    if (!ATTN_IN(h0 + rr < Hq, 3)) continue;  // checked build, site 3: the output row
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) M = fmaxf(M, red_ml[w][rr][0]);
@@ -389,6 +400,7 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(
     int table_max_pos, int Hq, int n_split, void* __restrict__ o, float* __restrict__ lse) {
   constexpr int kGroup = 8;  // partials whose loads are in flight together
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  if (!ATTN_IN(h < Hq && d < D, 4)) return;  // checked build, site 4: the merged row
   const int64_t base = ((int64_t)b * Hq + h) * n_split;
   // One pass over the splits, kGroup at a time, rescaling the running sum to each group's max.
   float M = -INFINITY, Lsum = 0.f, acc = 0.f;
@@ -480,6 +492,8 @@ hipError_t go_w(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+ATTN_CHECK_READER(checked_word_decode)
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t st) {
   // more than 16 query heads per KV head: the shared-tile kernel (its byte offsets are 32-bit)

@@ -148,6 +148,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   const int kend0 = min(split * chunk + chunk, L);
   const int kend = wstart < kend0 ? kend0 : 0;   // nothing visible in this split: empty
   const int nt = kend > kbeg ? (kend - kbeg + kTileKeys - 1) / kTileKeys : 0;
+  // checked build, site 0: the workgroup's (sequence, KV head, split, super-group) and key range
+  if (!ATTN_IN(b < B && hkv < Hkv && split < n_split && sg < n_super && kbeg >= 0 && kend <= S_max, 0)) return;
 
   // ---- HBM -> LDS: wave-load i of this wave fills chunks [(i * NW + wave) * 64, +64) of the
   // tile; lane L's chunk C holds logical chunk swz(r, C % NCH) of tile row r = C / NCH, read from
@@ -179,7 +181,8 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
       const int k0c = max(min(max(kbeg + t * kTileKeys, wstart), kend - 1), 0);
       const int j0 = wave_uniform(k0c >> bs_log2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ids[i] = btr[min(j0 + i, jmax)];  // clamped where used
+      for (int i = 0; i < 4; ++i)  // (clamped where used; checked build, site 2: inside the table row)
+        ids[i] = btr[ATTN_IN(min(j0 + i, jmax) < max_blocks, 2) ? min(j0 + i, jmax) : 0];
     }
   };
   auto issue = [&](int t, uint16_t* stage, uint16_t* vstage, const int (&ids)[4]) {
@@ -200,7 +203,9 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
       } else {
         row = (uint32_t)key;
       }
-      const uint32_t off = (row * D + dma_elem[i]) * 2 + dead;
+      uint32_t off = (row * D + dma_elem[i]) * 2 + dead;
+      // checked build, site 1: a live load's chunk inside the resource (else it moves nothing)
+      off = ATTN_IN(dead != 0u || (uint64_t)off + 16 <= kv_bytes, 1) ? off : kDeadOffset;
       ATTN_LDS void* lk = (ATTN_LDS void*)(stage + (i * NW + wave) * 512);
       ATTN_LDS void* lv = (ATTN_LDS void*)(vstage + (i * NW + wave) * 512);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lk, 16, (int)off, 0, 0, kLoadAux);
@@ -418,7 +423,7 @@ __global__ __launch_bounds__(2 * HG * 64) void decode_wide_kernel(
   const float s0 = M == -INFINITY ? 0.f : fast_exp2(m_run - M);
   const float s1 = M == -INFINITY ? 0.f : fast_exp2(m1 - M);
   const float Lsum = l_run * s0 + l1 * s1;
-  const bool valid = qvalid;
+  const bool valid = qvalid && ATTN_IN(h0 + i16 < Hq, 3);  // checked build, site 3: the output row
   const int h = h0 + i16;
   if constexpr (WHOLE) {
     const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
@@ -509,6 +514,8 @@ hipError_t go_d(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
+
+ATTN_CHECK_READER(checked_word_decode_wide)
 
 bool decode_wide_fits(const DecodeArgs& a) {
   if (a.Hq / a.Hkv <= 16) return false;

@@ -112,6 +112,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int b = rem / Hkv;
   const int hkv = rem % Hkv;
   const int h = hkv * G + gq;
+  // checked build, site 0: the workgroup's (batch, head, query block) and the key row counts
+  if (!ATTN_IN(b < B && h < Hq && hkv < Hkv && qblock * BM < Sq && Sk >= 1 && Sk <= k_rows && Sk <= v_rows, 0))
+    return;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -172,7 +175,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
         int r = dma_r0 + ROWS_PER_LOAD * i;
         asm volatile("" : "+v"(r));
         const int rr = min(r, Sk - 1 - k0);
-        const uint32_t off = dma_base + LOAD_BYTES * i - (uint32_t)((r - rr) * D * 2);
+        uint32_t off = dma_base + LOAD_BYTES * i - (uint32_t)((r - rr) * D * 2);
+        // checked build, site 1: the tail tile's source chunk lies within rows [k0, Sk)
+        off = ATTN_IN(off + 16 <= (uint32_t)(Sk - k0) * D * 2, 1) ? off : 0u;
         const void* g = base + off;
         ATTN_LDS void* l = (ATTN_LDS void*)(dst_tile + (i * NW + wave) * 512);
         __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
@@ -185,7 +190,11 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   // four row bits, which kb and s do not change, so those enter as immediate offsets.
   int kaddr[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) kaddr[ks] = (l32 * D + swz<D>(l32, 2 * ks + hl) * 8) * 2;
+  for (int ks = 0; ks < KS; ++ks) {
+    kaddr[ks] = (l32 * D + swz<D>(l32, 2 * ks + hl) * 8) * 2;
+    // checked build, site 2: both 32-key blocks' operands inside the tile
+    kaddr[ks] = ATTN_IN(kaddr[ks] >= 0 && kaddr[ks] + 32 * D * 2 + 16 <= TILE_ELEMS * 2, 2) ? kaddr[ks] : 0;
+  }
   int vaddr[DB][2];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -194,6 +203,9 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       const int vr = 8 * tg + 4 * hl + (i16 >> 2);
       const int lc = 4 * db + 2 * (g16 & 1) + ((i16 & 3) >> 1);
       vaddr[db][tg] = (vr * D + swz<D>(vr, lc) * 8 + 4 * (i16 & 1)) * 2;
+      // checked build, site 2: the farthest row the reads add (48 rows on) inside the tile
+      vaddr[db][tg] = ATTN_IN(vaddr[db][tg] >= 0 && vaddr[db][tg] + 48 * D * 2 + 8 <= TILE_ELEMS * 2, 2)
+                          ? vaddr[db][tg] : 0;
     }
 
   // fused-mode staging (bf16 K + its coefficient rows)
@@ -205,7 +217,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + NT * i;
         const int r = c / NCH, cc = c % NCH;
-        const int key = min(k0 + r, Sk - 1);
+        int key = min(k0 + r, Sk - 1);
+        key = ATTN_IN(key >= 0 && key < k_rows && cc < NCH, 3) ? key : 0;  // checked build, site 3
         kst[i] = *reinterpret_cast<const u32x4*>(kg + (int64_t)key * D + cc * 8);
         const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)(pos0 + key) * (D / 2) + cc * 4);
         tst[i][0] = tp[0];
@@ -574,7 +587,15 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   if constexpr (KMODE == KMODE_PREROT) {
     uint32_t acc = q_scaled ? 1u : 0u;
     const uintptr_t lo = reinterpret_cast<uintptr_t>(kexp_head + t_first * kBN) & ~(uintptr_t)15;
-    const uintptr_t hi = (reinterpret_cast<uintptr_t>(kexp_head + key_end) + 15) & ~(uintptr_t)15;
+    uintptr_t hi = (reinterpret_cast<uintptr_t>(kexp_head + key_end) + 15) & ~(uintptr_t)15;
+    // checked build, site 5: the words read lie inside the exponent area (else: no words read,
+    // and the workgroup takes the scaled loop, which reads the bytes one by one)
+    if (!ATTN_IN(lo >= reinterpret_cast<uintptr_t>(kexp) &&
+                     hi <= reinterpret_cast<uintptr_t>(kexp) + ((size_t)B * Hkv * k_rows + 255) / 256 * 256,
+                 5)) {
+      hi = lo;
+      acc = 1u;
+    }
     for (uintptr_t p = lo + 16 * (uintptr_t)tid; p < hi; p += 16 * NT) {
       const u32x4 w = *reinterpret_cast<const u32x4*>(p);
       acc |= w[0] | w[1] | w[2] | w[3];
@@ -598,7 +619,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
 
   // ---- finalize ----
   const float l_tot = l_run + swap_halves(l_run);
-  if (row < Sq) {
+  // checked build, site 6: the output row
+  if (row < Sq && ATTN_IN(row >= 0 && ((int64_t)b * Hq + h) * Sq + row < (int64_t)B * Hq * Sq, 6)) {
     const float inv = 1.0f / l_tot;
     const int64_t orow = (((int64_t)b * Hq + h) * Sq + row) * D;
 #pragma unroll
@@ -666,6 +688,8 @@ size_t prefill_workspace_bytes(int B, int Hkv, int S, int D) {
   const size_t exps = ((size_t)B * Hkv * S + 255) / 256 * 256;
   return prefill_kexp_offset(B, Hkv, S, D) + exps;
 }
+
+ATTN_CHECK_READER(checked_word_prefill_bf16)
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t st) {
   return a.D == 64 ? dispatch_d<64>(a, st) : dispatch_d<128>(a, st);

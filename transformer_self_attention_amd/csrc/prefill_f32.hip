@@ -37,6 +37,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
   const int kvh = h / (Hq / Hkv);
   const int row = qb * kRows + r;
   const int row_c = row < S ? row : S - 1;
+  // checked build, site 0: the workgroup's head, KV head and query block
+  if (!ATTN_IN(h < Hq && kvh < Hkv && qb * kRows < S && Hq % Hkv == 0, 0)) return;
 
   const float* qrow = q + (((int64_t)b * Hq + h) * S + row_c) * D + half * H;
   float qv[H];
@@ -131,6 +133,8 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(
 }
 
 }  // namespace
+
+ATTN_CHECK_READER(checked_word_prefill_f32)
 
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t st) {
   dim3 grid((a.S + kRows - 1) / kRows, a.Hq, a.B);

@@ -150,6 +150,12 @@ __global__ __launch_bounds__(256) void rope_apply_kernel(const void* x, void* ou
     const int64_t rem = idx - group * per_group;
     const int s = (int)(rem / lanes_per_row);
     const int p0 = (int)(rem - (int64_t)s * lanes_per_row) * PPT;  // first pair of this lane
+    // checked build, site 0: the last element of the last row block this lane touches
+    if (!ATTN_IN(s < S && p0 + PPT <= half &&
+                     ((group * HPT + min<int64_t>(HPT, bh_count - group * HPT) - 1) * S + s) * D + 2 * (p0 + PPT) <=
+                         bh_count * bh_stride,
+                 0))
+      continue;
     const float2* tr = table + (int64_t)(pos0 + s) * half + p0;
     float cs[2 * PPT];
 #pragma unroll
@@ -229,6 +235,11 @@ __global__ __launch_bounds__(256) void rope_k_f16_kernel(const uint16_t* __restr
     const int64_t bh0 = group * HPT;
     const int64_t base = (bh0 * S + s) * D + cc * 8;
     const int nh = bh_count - bh0 < HPT ? (int)(bh_count - bh0) : HPT;
+    // checked build, site 1: the last key element and exponent byte of this lane's row blocks
+    if (!ATTN_IN(s < S && cc < NCH && base + (nh - 1) * bh_stride + 8 <= bh_count * bh_stride &&
+                     (bh0 + nh - 1) * S + s < bh_count * S,
+                 1))
+      continue;
     // rotate, then scale the row by its exponent and store it as fp16
     auto rotate_store = [&](const u32x4 w, int hh) {
       float r[8];
@@ -275,6 +286,8 @@ static hipError_t rotate_keys(const void* k, void* k_rot, int64_t rows, int S, i
                      reinterpret_cast<const float2*>(table));
   return hipGetLastError();
 }
+
+ATTN_CHECK_READER(checked_word_rope)
 
 hipError_t launch_rotate_keys_f16(const void* k, void* k_rot, int B, int Hkv, int S, int D, int pos0,
                                   const float* table, hipStream_t st) {

@@ -24,6 +24,7 @@ ATTN_F32, ATTN_BF16 = 0, 1
 EXPORTED = (
     "attn_version",
     "attn_status_string",
+    "attn_checked_sites",
     "attn_rope_table_bytes",
     "attn_rope_table_init",
     "attn_rope_table_init_scaled",
@@ -59,6 +60,8 @@ def _load():
     vp, i32, sz, fp = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p
     lib.attn_version.restype = i32
     lib.attn_version.argtypes = []
+    lib.attn_checked_sites.restype = i32
+    lib.attn_checked_sites.argtypes = [vp, i32]
     lib.attn_status_string.restype = ctypes.c_char_p
     lib.attn_status_string.argtypes = [i32]
     lib.attn_rope_table_bytes.restype = sz
@@ -118,6 +121,15 @@ def raw():
 
 def status_string(status: int) -> str:
     return _lib.attn_status_string(int(status)).decode()
+
+
+def checked_sites():
+    """Checked build only: the words of failed index checks per source file (rope, cache,
+    prefill_bf16, prefill_f32, decode, decode_wide; bit i = check site i), cleared by the read;
+    None from a normal build.  Blocking: synchronize the device first."""
+    words = (ctypes.c_uint * 8)()
+    n = int(_lib.attn_checked_sites(words, 8))
+    return None if n < 0 else [int(words[i]) for i in range(n)]
 
 
 def version() -> int:
