@@ -10,7 +10,10 @@
 // CU):
 //  * Each wave owns 32 query rows.  Its Q rows sit in registers as the B operand of a 32x32x16
 //    MFMA: rotated in fp32, scaled by log2(e)/sqrt(D) and rounded to fp16 when RoPE is on; raw
-//    bf16 (exact) when it is off.
+//    bf16 (exact) when it is off.  fp16 rows (queries and keys) that would reach 2^15 are scaled
+//    by a power of two first (f16_row_exponent), and the scores of tiles holding such rows are
+//    scaled back in fp32; each workgroup checks its key range once and runs a key loop without
+//    that test when no row there is scaled.
 //  * Keys arrive in tiles of 64, double-buffered in LDS with an XOR swizzle of 16-byte chunks
 //    (bank-conflict-free operand reads).  Three ways to fill the K tile:
 //      KMODE_PREROT  keys already rotated to fp16 by a one-pass kernel (workspace given): K and V
