@@ -395,13 +395,18 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           (CAUSAL && (k0 + kBN - 1 > qw + coff || (WIN && k0 < qw + kRowsPerWave - 1 + coff - window))) ||
           (k0 + kBN > Sk);
       if (need_mask) {
+        // score (kb, r) belongs to key k0 + 4*hl + c with c = kb*32 + 8*(r>>2) + (r&3) fixed at
+        // compile time: it is visible when lo <= c <= hi, two bounds per lane
+        const int base = k0 + 4 * hl;
+        int hi = Sk - 1 - base;
+        if constexpr (CAUSAL) hi = min(hi, row + coff - base);
+        const int lo = (CAUSAL && WIN) ? row + coff - window - base : 0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = k0 + kb * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-            if ((CAUSAL && (key > row + coff || (WIN && key < row + coff - window))) || key >= Sk)
-              sacc[kb][r] = -INFINITY;
+            const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+            if (c > hi || (CAUSAL && WIN && c < lo)) sacc[kb][r] = -INFINITY;
           }
       }
       bf16x8 pf[2][2];
@@ -541,8 +546,8 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
       if constexpr (QK_BF16) qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
     if constexpr (!QK_BF16) {
-      // the row rotated and scaled by log2(e)/sqrt(D): once for the row's exponent, once more to
-      // round it (scaled by 2^-qa) to fp16
+      // the row rotated and scaled by log2(e)/sqrt(D), its exponent, then the row (scaled by 2^-qa
+      // when some row of the wave has one) rounded to fp16
       auto rotated = [&](int ks, float (&x)[8]) __attribute__((always_inline)) {
         const int d0 = 16 * ks + 8 * hl;
         const u32x4 w = *reinterpret_cast<const u32x4*>(qrow + d0);
@@ -559,23 +564,26 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
           x[2 * p + 1] = (x0 * s + x1 * c) * c_log2;
         }
       };
+      float xq[KS][8];
       float qmax = 0.f;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-        rotated(ks, x);
+        rotated(ks, xq[ks]);
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qmax = fmaxf(qmax, fabsf(x[t]));
+        for (int t = 0; t < 8; ++t) qmax = fmaxf(qmax, fabsf(xq[ks][t]));
       }
       qa = f16_row_exponent(fmaxf(qmax, swap_halves(qmax)));
       q_scaled = __builtin_amdgcn_ballot_w64(qa != 0) != 0;
+      if (q_scaled) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        float x[8];
-        rotated(ks, x);
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)ldexpf(x[t], -qa);
+          for (int t = 0; t < 8; ++t) xq[ks][t] = ldexpf(xq[ks][t], -qa);
       }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 8; ++t) qf[ks][t] = (_Float16)xq[ks][t];
     }
   }
 
