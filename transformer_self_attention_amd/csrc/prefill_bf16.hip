@@ -17,7 +17,8 @@
 //  * Keys arrive in tiles of 64, double-buffered in LDS with an XOR swizzle of 16-byte chunks
 //    (bank-conflict-free operand reads).  Three ways to fill the K tile:
 //      KMODE_PREROT  keys already rotated to fp16 by a one-pass kernel (workspace given): K and V
-//                    tiles go HBM -> LDS with global_load_lds_dwordx4, no register staging;
+//                    tiles go HBM -> LDS with no register staging (buffer loads to LDS; the
+//                    tail tile with global_load_lds_dwordx4);
 //      KMODE_FUSED   RoPE fused into the K tile load: bf16 K and the coefficient rows are staged
 //                    in registers, rotated in fp32, stored to LDS as fp16;
 //      KMODE_RAW     no RoPE: bf16 K straight to LDS; Q.K^T on bf16 operands (exact products),
