@@ -158,14 +158,16 @@ def test_prefill_bf16_ragged(lib, B, Hq, Hkv, S, D, causal, out, mode):
 
 
 def test_prefill_mha_config(lib):
-    """MHA workload at full size: B=4, H=32, S=2048, D=128, bf16, every row checked."""
+    """MHA workload at full size: B=4, H=32, S=2048, D=128, bf16, every row checked.
+    Both key paths: rotated once into a workspace (the benchmarked path) and fused per tile."""
     wl = inputs.WORKLOADS["mha"]
     banner("prefill MHA B=4 H=32 S=2048 D=128 (full config, all rows)")
     p = inputs.make_prefill(wl)
-    o, lse = run_prefill(lib, p)
     ref, ref_lse = oracle_rows(p)
-    assert_bf16_parity(to_np(o), ref, "mha o")
-    assert err_stats(to_np(lse), ref_lse)[0] < 2e-2
+    for ws in (True, False):
+        o, lse = run_prefill(lib, p, workspace=ws)
+        assert_bf16_parity(to_np(o), ref, f"mha o (workspace={ws})")
+        assert err_stats(to_np(lse), ref_lse)[0] < 2e-2
 
 
 def test_prefill_gqa_config(lib):
