@@ -13,7 +13,7 @@ One step = one pass of the hot path over the workload's synthetic batch:
     per (sequence, KV head) streams the whole cache).
   * MHA (sub-object ``mha_prefill``): B=4, H=32, S=2048, D=128 prefill, same step.
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
-    key rows scaled by 8.
+    key rows scaled by 8, written as fp32 output (the output held to the parity bars there).
   * paged decode (sub-object ``paged_decode``): the decode workload with the cache cut into
     16-token blocks scattered over a pool in a seeded random order; one attn_decode_paged call.
   * sliding window (sub-objects ``swa_prefill``, ``swa_decode``): the long-context prefill and
