@@ -6,7 +6,8 @@ case captures one step on preallocated buffers, then replays it several times; b
 replay new inputs are copied into the captured buffers eagerly and the stream is synchronised,
 and each replay must equal, bit for bit, the same call made eagerly on the same inputs.  Cases:
 the prefill step (key rotation into a workspace + attention), a decode split over the cache with
-its merge pass, and the multi-query decode (wide kernel + merge).
+its merge pass, the multi-query decode (wide kernel + merge), and a serving step against a paged
+pool (a chunk appended into its blocks and attended, then a split decode against the pool).
 """
 
 import pytest
@@ -96,3 +97,60 @@ def test_graph_decode_with_merge(lib, Hq, Hkv, n_split):
 
     ws2 = torch.empty_like(ws)
     _replays(g, load, out, lambda: lib.decode(q, kc, vc, cl, qp, tab, n_split=n_split, workspace=ws2))
+
+
+def test_graph_serving_step_paged(lib):
+    """One serving step in one graph: a 100-token chunk at pos0 = 300 appended into a shuffled
+    16-token block pool and attended (three launches), then the next token's decode against the
+    pool (split + merge).  Each replay must match the eager step in both outputs and in every
+    byte of the pools."""
+    B, Hq, Hkv, D, bs = 2, 16, 4, 128, 16
+    S_max, pos0, Sq = 512, 300, 100
+    banner(f"HIP graph: serving step, chunk Sq={Sq} at pos0={pos0} into a paged pool + paged decode, 4 replays")
+    max_blocks = S_max // bs
+    num_blocks = B * max_blocks + 3
+    g0 = torch.Generator(device="cuda").manual_seed(41)
+
+    def rnd(shape, g=g0):
+        return torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+
+    k_pages, v_pages = rnd((num_blocks, Hkv, bs, D)), rnd((num_blocks, Hkv, bs, D))
+    perm = torch.randperm(num_blocks, generator=torch.Generator().manual_seed(5))[:B * max_blocks]
+    block_table = perm.view(B, max_blocks).to(torch.int32).cuda()
+    q_chunk, k_chunk, v_chunk = rnd((B, Hq, Sq, D)), rnd((B, Hkv, Sq, D)), rnd((B, Hkv, Sq, D))
+    q1 = rnd((B, Hq, 1, D))
+    cache_len = torch.full((B,), pos0 + Sq, dtype=torch.int32, device="cuda")
+    q_pos = cache_len.clone()
+    tab = lib.make_rope_table(S_max + 1, D)
+    assert lib.decode_num_splits(B, Hq, Hkv, max_blocks * bs, D) > 1, "the decode must take the merge pass"
+
+    def buffers():
+        return (torch.empty(lib.prefill_chunk_paged_workspace_bytes(B, Hkv, pos0, Sq, D), dtype=torch.uint8,
+                            device="cuda"),
+                torch.empty(lib.decode_workspace_bytes(B, Hq, Hkv, max_blocks * bs, D), dtype=torch.uint8,
+                            device="cuda"),
+                torch.empty_like(q_chunk), torch.empty_like(q1))
+
+    def step(ws_c, ws_d, o_c, o_d):
+        lib.prefill_chunk_paged(q_chunk, k_chunk, v_chunk, k_pages, v_pages, block_table, pos0, tab, out=o_c,
+                                workspace=ws_c)
+        lib.decode_paged(q1, k_pages, v_pages, block_table, cache_len, q_pos, tab, out=o_d, workspace=ws_d)
+
+    cap = buffers()
+    g = _capture(lambda: step(*cap))
+    eager = buffers()
+    for i in range(4):
+        gi = torch.Generator(device="cuda").manual_seed(300 + i)
+        for t in (q_chunk, k_chunk, v_chunk, q1):
+            t.copy_(rnd(t.shape, gi))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got_c, got_d = cap[2].clone(), cap[3].clone()
+        kp, vp = k_pages.clone(), v_pages.clone()
+        step(*eager)   # appends the same rows again: the pools must not change
+        torch.cuda.synchronize()
+        assert torch.equal(got_c, eager[2]), f"replay {i}: chunk output differs from the eager call"
+        assert torch.equal(got_d, eager[3]), f"replay {i}: decode output differs from the eager call"
+        assert torch.equal(kp, k_pages) and torch.equal(vp, v_pages), f"replay {i}: pools differ"
+        assert torch.isfinite(got_c.float()).all() and torch.isfinite(got_d.float()).all()
