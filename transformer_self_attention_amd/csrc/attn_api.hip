@@ -13,7 +13,9 @@
 namespace {
 
 constexpr int kVersion = 20100;  // 2.1.0
+#ifdef ATTN_CHECKED
 constexpr int kCheckedWords = 6;  // source files with index checks (attn_checked_sites)
+#endif
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
