@@ -27,6 +27,7 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    "-Wextra",
     "-Wno-unused-value",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE,
