@@ -71,7 +71,7 @@ typedef enum {
 
 /* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
  * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys; 2.1.0:
- * attn_checked_sites. */
+ * attn_checked_sites; 2.2.0: attn_prefill_chunk_varpos. */
 int attn_version(void);
 
 /* Index checks of a checked build (the library compiled with ATTN_CHECKED; a debugging aid, not
@@ -249,6 +249,29 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
                                int Hkv, int Sq, int S_max, int D, int pos0, int window,
                                const float* rope_table, int table_max_pos, void* workspace,
                                size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_prefill_chunk_varpos: attn_prefill_chunk for a batch whose sequences have reached
+ * different lengths (same page sections): sequence b's chunk of Sq tokens sits at positions
+ * p_b .. p_b+Sq-1, p_b = pos0[b], and is appended to its cache rows [p_b, p_b + Sq); its
+ * queries attend to cache rows j <= p_b + i (and, with a window W >= 0, j >= p_b + i - W).
+ *
+ * pos0: device int32 [B], 4-byte aligned, read on the device only.  Each value must lie in
+ *   [0, pos0_max].  A sequence whose value lies outside gets NaN output rows (and NaN LSE),
+ *   and its cache rows are left unchanged; the other sequences are not affected.
+ * pos0_max: host int >= 0, the largest start the call allows: pos0_max + Sq <= S_max, and
+ *   with RoPE pos0_max + Sq <= table_max_pos.
+ * workspace: required with RoPE: at least attn_prefill_workspace_bytes(B, Hkv, pos0_max + Sq, D)
+ *   bytes, 16-byte aligned, contents irrelevant.
+ * With every pos0[b] equal to p the result is attn_prefill_chunk's with pos0 = p, bit for bit.
+ * Other arguments, layouts, the support matrix and the errors as in attn_prefill_chunk (with
+ * pos0_max in place of pos0); also ATTN_ERR_INVALID_ARG for a null or misaligned pos0.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_prefill_chunk_varpos(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* pos0, int pos0_max, void* o, float* lse,
+                                      attn_dtype out_dt, int B, int Hq, int Hkv, int Sq, int S_max, int D,
+                                      int window, const float* rope_table, int table_max_pos,
+                                      void* workspace, size_t workspace_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_prefill_chunk_paged: attn_prefill_chunk against a paged KV cache, the block pool of

@@ -35,7 +35,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert lib.version() == 20100
+    assert lib.version() == 20200
     assert lib.checked_sites() is None     # the normal build has no index checks
     assert lib.status_string(OK) == "ATTN_OK"
     for s in (INV, UNSUP, lib.ATTN_ERR_HIP):
@@ -210,6 +210,35 @@ def _chunk(**kw):
 ])
 def test_prefill_chunk_rejects(kw, code):
     assert _chunk(**kw) == code
+
+
+def _chunk_varpos(**kw):
+    a = dict(q=A, kn=A, vn=A, kc=A, vc=A, p0=A, p0max=50, o=A, lse=None, out_dt=BF16, B=2, Hq=8, Hkv=2, Sq=100,
+             S_max=300, D=128, window=-1, table=A, tmax=300, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.prefill_workspace_bytes(a["B"], a["Hkv"], max(a["p0max"], 0) + a["Sq"], a["D"])
+    return lib.raw().attn_prefill_chunk_varpos(a["q"], a["kn"], a["vn"], a["kc"], a["vc"], a["p0"], a["p0max"],
+                                               a["o"], a["lse"], a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["Sq"],
+                                               a["S_max"], a["D"], a["window"], a["table"], a["tmax"], a["ws"],
+                                               a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kn=None), INV), (dict(vn=None), INV), (dict(kc=None), INV),
+    (dict(vc=None), INV), (dict(o=None), INV), (dict(p0=None), INV), (dict(p0=P(0x10002)), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(S_max=0), INV),
+    (dict(D=0), INV), (dict(p0max=-1), INV), (dict(Hq=8, Hkv=3), INV),
+    (dict(p0max=201), INV),                                  # pos0_max + Sq > S_max
+    (dict(tmax=149), INV),                                   # table too short for the last allowed position
+    (dict(ws=None), INV), (dict(ws=MIS), INV),
+    (dict(wsb=lib.prefill_workspace_bytes(2, 2, 150, 128) - 1), INV),
+    (dict(q=MIS), INV), (dict(kc=MIS), INV), (dict(vn=MIS), INV), (dict(lse=MIS), INV),
+    (dict(table=MIS), INV), (dict(D=65), INV), (dict(out_dt=5), INV),
+    (dict(D=96), UNSUP), (dict(D=96, table=None, ws=None), UNSUP),
+])
+def test_prefill_chunk_varpos_rejects(kw, code):
+    assert _chunk_varpos(**kw) == code
 
 
 def _chunk_paged(**kw):

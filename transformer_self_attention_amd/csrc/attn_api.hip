@@ -12,7 +12,7 @@
 
 namespace {
 
-constexpr int kVersion = 20100;  // 2.1.0
+constexpr int kVersion = 20200;  // 2.2.0
 #ifdef ATTN_CHECKED
 constexpr int kCheckedWords = 6;  // source files with index checks (attn_checked_sites)
 #endif
@@ -340,6 +340,49 @@ attn_status attn_prefill_chunk(const void* q, const void* k_new, const void* v_n
   a.workspace = nullptr;
   a.Sk = Sk; a.k_rows = rope_table ? Sk : S_max; a.v_rows = S_max; a.coff = pos0;
   a.window = kw;
+  return from_hip(attn::launch_prefill_cache(a, st));
+}
+
+attn_status attn_prefill_chunk_varpos(const void* q, const void* k_new, const void* v_new, void* k_cache,
+                                      void* v_cache, const int32_t* pos0, int pos0_max, void* o, float* lse,
+                                      attn_dtype out_dt, int B, int Hq, int Hkv, int Sq, int S_max, int D,
+                                      int window, const float* rope_table, int table_max_pos,
+                                      void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !o || !pos0) return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || S_max < 1 || D < 1 || pos0_max < 0) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)pos0_max + Sq > (int64_t)S_max) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) ||
+      !aligned16(v_cache) || !aligned16(o) || (lse && !aligned16(lse)) || (reinterpret_cast<uintptr_t>(pos0) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0_max, Sq) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  const int Sk_max = pos0_max + Sq;
+  if (rope_table && (!workspace || !aligned16(workspace) ||
+                     workspace_bytes < attn::prefill_workspace_bytes(B, Hkv, Sk_max, D)))
+    return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * Sq > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+
+  hipStream_t st = (hipStream_t)stream;
+  void* k16 = rope_table ? workspace : nullptr;
+  const int kw = kernel_window(window);
+  // each sequence's start is read on the device; pos0_max bounds them and sizes the fp16 rows
+  const hipError_t e = attn::launch_cache_append_varpos(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max,
+                                                        D, pos0_max, pos0, kw, rope_table, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  attn::PrefillArgs a;
+  a.q = q; a.k = rope_table ? k16 : k_cache; a.v = v_cache; a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = Sq; a.D = D;
+  a.causal = true;
+  a.pos0 = pos0_max;
+  a.table = rope_table;
+  a.workspace = nullptr;
+  a.Sk = Sk_max; a.k_rows = rope_table ? Sk_max : S_max; a.v_rows = S_max; a.coff = pos0_max;
+  a.window = kw;
+  a.pos0_dev = pos0;
   return from_hip(attn::launch_prefill_cache(a, st));
 }
 

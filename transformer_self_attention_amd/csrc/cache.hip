@@ -45,17 +45,22 @@ __device__ __forceinline__ int to_f16_row(const u32x4 w, u32x4& h) {
   return e;
 }
 
-template <int D, bool ROPE>
+// VARPOS: chunks at per-sequence positions.  The grid then covers rows [0, pos0 + Sq) of every
+// (batch, KV head), pos0 being the largest start allowed and the k16 / kexp row count; sequence
+// b's chunk starts at p = pos0_dev[b], and only its rows [p, p + Sq) (with RoPE: from its own
+// conv_first, the tile of p - window) are written.  A sequence whose p lies outside [0, pos0]
+// is left untouched.
+template <int D, bool ROPE, bool VARPOS>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
     uint16_t* __restrict__ k_cache, uint16_t* __restrict__ v_cache, uint16_t* __restrict__ k16,
-    uint8_t* __restrict__ kexp, int64_t n_bh, int Sq, int S_max, int pos0, int conv_first,
-    const float2* __restrict__ table) {
+    uint8_t* __restrict__ kexp, int64_t n_bh, int Sq, int S_max, int pos0_in, int conv_first,
+    const float2* __restrict__ table, const int32_t* __restrict__ pos0_dev, int Hkv, int window) {
   constexpr int NCH = D / 8;  // 16-byte chunks per row
   // rows handled per (batch, KV head): [first, pos0 + Sq); with RoPE the earlier rows from
   // conv_first on (those a sliding window can still see) are converted to fp16
-  const int first = ROPE ? conv_first : pos0;
-  const int Sk = pos0 + Sq;
+  const int first = VARPOS ? 0 : ROPE ? conv_first : pos0_in;
+  const int Sk = pos0_in + Sq;  // rows per (batch, KV head) of k16 and kexp
   const int nrows = Sk - first;
   const int64_t n = n_bh * nrows * NCH;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
@@ -65,6 +70,14 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     const int s = first + (int)(rr % nrows);
     const int64_t bh = rr / nrows;
     const int64_t crow = (bh * S_max + s) * D + cc * 8;  // element offset in the cache
+    int pos0 = pos0_in;
+    if constexpr (VARPOS) {
+      // the NCH lanes of a row share s and bh, so they skip together (to_f16_row needs all of them)
+      pos0 = pos0_dev[bh / Hkv];
+      if (pos0 < 0 || pos0 > pos0_in) continue;
+      const int lo = !ROPE ? pos0 : window >= pos0 ? 0 : ((pos0 - window) / 64) * 64;
+      if (s < lo || s >= pos0 + Sq) continue;
+    }
     // checked build, site 0: the row in the cache, in the fp16 copy and in the chunk
     if (!ATTN_IN(bh < n_bh && s >= 0 && s < Sk && Sk <= S_max && (s < pos0 || s - pos0 < Sq), 0)) continue;
     if (s < pos0) {
@@ -101,27 +114,27 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
   }
 }
 
-template <int D>
+template <int D, bool VARPOS>
 hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* v_cache, void* k16,
                      int B, int Hkv, int Sq, int S_max, int pos0, int conv_first, const float* table,
-                     hipStream_t st) {
+                     const int32_t* pos0_dev, int window, hipStream_t st) {
   const int64_t n_bh = (int64_t)B * Hkv;
-  const int64_t rows = table ? (int64_t)(pos0 + Sq - conv_first) : (int64_t)Sq;
+  const int64_t rows = VARPOS ? (int64_t)(pos0 + Sq) : table ? (int64_t)(pos0 + Sq - conv_first) : (int64_t)Sq;
   const int64_t n = n_bh * rows * (D / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 workgroups per CU
   if (blocks < 1) blocks = 1;
   if (table)
-    hipLaunchKernelGGL((cache_append_kernel<D, true>), dim3((unsigned)blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((cache_append_kernel<D, true, VARPOS>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, (uint16_t*)k16,
                        static_cast<uint8_t*>(k16) + prefill_kexp_offset(B, Hkv, pos0 + Sq, D), n_bh, Sq,
-                       S_max, pos0, conv_first, reinterpret_cast<const float2*>(table));
+                       S_max, pos0, conv_first, reinterpret_cast<const float2*>(table), pos0_dev, Hkv, window);
   else
-    hipLaunchKernelGGL((cache_append_kernel<D, false>), dim3((unsigned)blocks), dim3(256), 0, st,
+    hipLaunchKernelGGL((cache_append_kernel<D, false, VARPOS>), dim3((unsigned)blocks), dim3(256), 0, st,
                        (const uint16_t*)k_new, (const uint16_t*)v_new, (uint16_t*)k_cache,
                        (uint16_t*)v_cache, (uint16_t*)nullptr, (uint8_t*)nullptr, n_bh, Sq, S_max, pos0, pos0,
-                       (const float2*)nullptr);
+                       (const float2*)nullptr, pos0_dev, Hkv, window);
   return hipGetLastError();
 }
 
@@ -235,10 +248,19 @@ hipError_t launch_cache_append_paged(const void* k_new, const void* v_new, void*
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
                                int conv_first, const float* table, hipStream_t st) {
-  return D == 64 ? append_go<64>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
-                                 table, st)
-                 : append_go<128>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
-                                  table, st);
+  return D == 64 ? append_go<64, false>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
+                                        table, nullptr, 0, st)
+                 : append_go<128, false>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0, conv_first,
+                                         table, nullptr, 0, st);
+}
+
+hipError_t launch_cache_append_varpos(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                      void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0_max,
+                                      const int32_t* pos0_dev, int window, const float* table, hipStream_t st) {
+  return D == 64 ? append_go<64, true>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0_max, 0,
+                                       table, pos0_dev, window, st)
+                 : append_go<128, true>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0_max, 0,
+                                        table, pos0_dev, window, st);
 }
 
 }  // namespace attn

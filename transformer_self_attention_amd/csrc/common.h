@@ -156,6 +156,10 @@ struct PrefillArgs {
   int Sk, k_rows, v_rows, coff;
   // Sliding window: key j is visible to row i only if j >= i + coff - window (no window: 1 << 30).
   int window;
+  // Chunks at per-sequence positions (chunked prefill only): sequence b's chunk starts at
+  // pos0_dev[b] (device int32 [B]), which then replaces pos0 and coff, and Sk = pos0_dev[b] + S;
+  // coff holds the largest start allowed.  nullptr: one position for the batch.
+  const int32_t* pos0_dev = nullptr;
 };
 
 // Rotated keys as fp16 [B, Hkv, S, D], then one exponent byte per key row [B, Hkv, S] at byte
@@ -175,6 +179,12 @@ hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hi
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
                                void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0,
                                int conv_first, const float* table, hipStream_t st);
+// The same with per-sequence chunk starts pos0_dev[b] (device int32 [B], each in [0, pos0_max]):
+// k16 holds pos0_max + Sq rows per (batch, KV head); window (kernel form, 1 << 30: none) sets
+// each sequence's first fp16 row; a sequence whose start is out of range is not written.
+hipError_t launch_cache_append_varpos(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                                      void* k16, int B, int Hkv, int Sq, int S_max, int D, int pos0_max,
+                                      const int32_t* pos0_dev, int window, const float* table, hipStream_t st);
 // The same for a paged cache: pools [num_blocks, Hkv, 1 << bs_log2, D] and a block table
 // [B, max_blocks].  The new rows go into their blocks; rows [conv_first, pos0 + Sq) are also
 // gathered into k_ws (fp16 with RoPE, bf16 without) and v_ws (bf16), both [B*Hkv, pos0 + Sq, D]

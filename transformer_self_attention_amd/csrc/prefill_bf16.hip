@@ -69,13 +69,18 @@ __device__ __forceinline__ int swz(int r, int lc) {
 }
 
 // WIN: a sliding window is applied (causal only); without it the window code is compiled out.
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW, bool WIN>
+// VARPOS: chunks at per-sequence positions (causal only): sequence b's chunk starts at key row
+// p = pos0_dev[b], so its keys are rows [0, p + Sq), query row i sees key j <= i + p and sits at
+// RoPE position p + i; coff_in is the largest start allowed (the key rows the buffers hold).  A
+// start outside [0, coff_in] makes the workgroup write NaN rows instead of reading anything.
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, int NW, bool WIN, bool VARPOS>
 __global__ __attribute__((amdgpu_flat_work_group_size(NW * 64, NW * 64), amdgpu_waves_per_eu(NW / 2, NW / 2)))
 void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                          const uint16_t* __restrict__ v, void* __restrict__ o,
-                         float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Sk,
-                         int k_rows, int v_rows, int coff, int window, int pos0,
-                         const float2* __restrict__ table, const uint8_t* __restrict__ kexp) {
+                         float* __restrict__ lse, int B, int Hq, int Hkv, int Sq, int Sk_in,
+                         int k_rows, int v_rows, int coff_in, int window, int pos0_in,
+                         const float2* __restrict__ table, const uint8_t* __restrict__ kexp,
+                         const int32_t* __restrict__ pos0_dev) {
   constexpr int NT = NW * 64;                // threads per workgroup
   constexpr int NCH = D / 8;                 // 16-byte chunks per row
   constexpr int KS = D / 16;                 // MFMA k-steps over D
@@ -116,6 +121,27 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int b = rem / Hkv;
   const int hkv = rem % Hkv;
   const int h = hkv * G + gq;
+  int Sk = Sk_in, coff = coff_in, pos0 = pos0_in;
+  if constexpr (VARPOS) {
+    const int p = __builtin_amdgcn_readfirstlane(pos0_dev[b]);
+    if (p < 0 || p > coff_in) {
+      // no valid chunk position: the workgroup's output rows (and LSE) become NaN
+      const int r0 = qblock * BM, nr = min(BM, Sq - r0);
+      const int64_t obase = (((int64_t)b * Hq + h) * Sq + r0) * D;
+      for (int i = threadIdx.x; i < nr * D; i += NT) {
+        if constexpr (OUT_BF16)
+          reinterpret_cast<__bf16*>(o)[obase + i] = (__bf16)__builtin_nanf("");
+        else
+          reinterpret_cast<float*>(o)[obase + i] = __builtin_nanf("");
+      }
+      if (lse)
+        for (int i = threadIdx.x; i < nr; i += NT) lse[((int64_t)b * Hq + h) * Sq + r0 + i] = __builtin_nanf("");
+      return;
+    }
+    Sk = p + Sq;
+    coff = p;
+    pos0 = p;
+  }
   // checked build, site 0: the workgroup's (batch, head, query block) and the key row counts
   if (!ATTN_IN(b < B && h < Hq && hkv < Hkv && qblock * BM < Sq && Sk >= 1 && Sk <= k_rows && Sk <= v_rows, 0))
     return;
@@ -698,7 +724,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   }
 }
 
-template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, bool WIN>
+template <int D, bool CAUSAL, int KMODE, bool OUT_BF16, bool WIN, bool VARPOS = false>
 hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   constexpr int NW = kWavesStream;
   constexpr int BM = NW * kRowsPerWave;
@@ -710,10 +736,11 @@ hipError_t go(const PrefillArgs& a, const void* kptr, hipStream_t st) {
   const uint8_t* kexp = KMODE == KMODE_PREROT
                             ? static_cast<const uint8_t*>(kptr) + prefill_kexp_offset(a.B, a.Hkv, a.k_rows, D)
                             : nullptr;
-  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW, WIN>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((prefill_bf16_kernel<D, CAUSAL, KMODE, OUT_BF16, NW, WIN, VARPOS>), dim3((unsigned)blocks),
                      dim3(NW * 64), 0, st, (const uint16_t*)a.q, (const uint16_t*)kptr,
                      (const uint16_t*)a.v, a.o, a.lse, a.B, a.Hq, a.Hkv, a.S, a.Sk, a.k_rows,
-                     a.v_rows, a.coff, a.window, a.pos0, reinterpret_cast<const float2*>(a.table), kexp);
+                     a.v_rows, a.coff, a.window, a.pos0, reinterpret_cast<const float2*>(a.table), kexp,
+                     a.pos0_dev);
   return hipGetLastError();
 }
 
@@ -725,6 +752,16 @@ hipError_t dispatch_mode(const PrefillArgs& a, const void* kptr, hipStream_t st)
     return a.out_bf16 ? go<D, true, KMODE, true, false>(a, kptr, st) : go<D, true, KMODE, false, false>(a, kptr, st);
   }
   return a.out_bf16 ? go<D, false, KMODE, true, false>(a, kptr, st) : go<D, false, KMODE, false, false>(a, kptr, st);
+}
+
+// chunks at per-sequence positions (always causal)
+template <int D, int KMODE>
+hipError_t dispatch_varpos(const PrefillArgs& a, const void* kptr, hipStream_t st) {
+  if (a.window < kNoWindow)
+    return a.out_bf16 ? go<D, true, KMODE, true, true, true>(a, kptr, st)
+                      : go<D, true, KMODE, false, true, true>(a, kptr, st);
+  return a.out_bf16 ? go<D, true, KMODE, true, false, true>(a, kptr, st)
+                    : go<D, true, KMODE, false, false, true>(a, kptr, st);
 }
 
 template <int D>
@@ -756,6 +793,11 @@ hipError_t launch_prefill_prerotated(const PrefillArgs& a, const void* k_rot, hi
 }
 
 hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st) {
+  if (a.pos0_dev) {
+    if (a.table)
+      return a.D == 64 ? dispatch_varpos<64, KMODE_PREROT>(a, a.k, st) : dispatch_varpos<128, KMODE_PREROT>(a, a.k, st);
+    return a.D == 64 ? dispatch_varpos<64, KMODE_RAW>(a, a.k, st) : dispatch_varpos<128, KMODE_RAW>(a, a.k, st);
+  }
   if (a.table)
     return a.D == 64 ? dispatch_mode<64, KMODE_PREROT>(a, a.k, st) : dispatch_mode<128, KMODE_PREROT>(a, a.k, st);
   return a.D == 64 ? dispatch_mode<64, KMODE_RAW>(a, a.k, st) : dispatch_mode<128, KMODE_RAW>(a, a.k, st);

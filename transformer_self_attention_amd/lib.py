@@ -34,6 +34,7 @@ EXPORTED = (
     "attn_rotate_keys_f16",
     "attn_prefill_prerotated",
     "attn_prefill_chunk",
+    "attn_prefill_chunk_varpos",
     "attn_prefill_chunk_paged_workspace_bytes",
     "attn_prefill_chunk_paged",
     "attn_decode_workspace_bytes",
@@ -86,6 +87,9 @@ def _load():
     lib.attn_prefill_chunk.restype = i32
     lib.attn_prefill_chunk.argtypes = [vp, vp, vp, vp, vp, vp, fp, i32, i32, i32, i32, i32, i32, i32, i32,
                                        i32, fp, i32, vp, sz, vp]
+    lib.attn_prefill_chunk_varpos.restype = i32
+    lib.attn_prefill_chunk_varpos.argtypes = [vp, vp, vp, vp, vp, vp, i32, vp, fp, i32, i32, i32, i32, i32, i32,
+                                              i32, i32, fp, i32, vp, sz, vp]
     lib.attn_prefill_chunk_paged_workspace_bytes.restype = sz
     lib.attn_prefill_chunk_paged_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
     lib.attn_prefill_chunk_paged.restype = i32
@@ -421,6 +425,40 @@ def prefill_chunk(q, k_new, v_new, k_cache, v_cache, pos0, table=None, *, window
                                    _ptr(lse), _dt(out), B, Hq, Hkv, Sq, S_max, D, pos0, _win(window), _ptr(table),
                                    tmax, _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "attn_prefill_chunk")
+    return out
+
+
+def prefill_chunk_varpos(q, k_new, v_new, k_cache, v_cache, pos0, pos0_max, table=None, *, window=None,
+                         out=None, out_dtype=None, lse=None, workspace=None, stream=None):
+    """prefill_chunk() with a chunk start per sequence: pos0 is a device int32 [B] tensor (sequence
+    b's chunk goes to cache rows pos0[b] .. pos0[b]+Sq-1) and pos0_max a host bound on its values
+    (a sequence whose start lies outside [0, pos0_max] gets NaN rows and an untouched cache).
+    workspace: uint8 GPU tensor of >= prefill_workspace_bytes(B, Hkv, pos0_max + Sq, D) bytes,
+    needed with RoPE; allocated here when None."""
+    B, Hq, Hkv, Sq, D = _chunk_inputs(q, k_new, v_new)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, S_max, D]")
+    S_max = k_cache.shape[2]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, q.device)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+        _shape(t, (B, Hkv, S_max, D), n)
+    _need(pos0, "pos0", q.device)
+    if pos0.dtype != torch.int32 or pos0.numel() != B:
+        raise ValueError(f"pos0 must be int32 [{B}]")
+    out = _out(out, (B, Hq, Sq, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * Sq, q.device)
+    tmax = _table(table, D, q.device)
+    if tmax:
+        workspace = _scratch(workspace, prefill_workspace_bytes(B, Hkv, pos0_max + Sq, D), q.device, stream)
+    elif workspace is not None:
+        _need(workspace, "workspace", q.device)
+    _check(_lib.attn_prefill_chunk_varpos(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(pos0), int(pos0_max), _ptr(out), _ptr(lse), _dt(out), B, Hq, Hkv,
+                                          Sq, S_max, D, _win(window), _ptr(table), tmax, _ptr(workspace),
+                                          _nbytes(workspace), _stream(stream)),
+           "attn_prefill_chunk_varpos")
     return out
 
 
