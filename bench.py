@@ -25,7 +25,9 @@ One step = one pass of the hot path over the workload's synthetic batch:
     attn_prefill_chunk call (append the chunk's rotated keys and values to the cache, then the
     chunk's queries against cache rows [0, 8192) with the bottom-right causal mask); and
     (``paged_chunk_prefill``) the same chunk against the cache in 16-token blocks scattered over
-    a pool, one attn_prefill_chunk_paged call.
+    a pool, one attn_prefill_chunk_paged call; and (``varpos_chunk_prefill``) a batch of 4 with a
+    chunk start per sequence (0, 2048, 4096, 6144: the four chunks of an 8192-token prompt at
+    once), one attn_prefill_chunk_varpos call.
 
 Inputs are resident in HBM before timing starts.  W untimed warmup steps, then K timed steps
 bracketed by torch.cuda.synchronize(), timed with HIP events recorded on the stream the library
@@ -327,7 +329,27 @@ def bench_chunk(lib, inputs, wl, steps, warmup):
                       steps, warmup, heat=True)
     tf_p = wl.chunk_flops() / (ms_p * 1e-3) / 1e12
     log(f"[bench] paged chunk prefill: {ms_p:.4f} ms/step, {tf_p:.1f} TFLOP/s")
-    return {"c": c, "ms": ms, "tflops": tf, "ms_paged": ms_p, "tflops_paged": tf_p}
+    del kp, vp, pc
+    # chunk starts per sequence: a batch of 4 whose sequences sit at 0, 2048, 4096 and 6144 of the
+    # same 8192-row cache (the four chunks of an 8192-token prompt at once); the chunk workload's
+    # draws repeated over the batch
+    starts = [i * wl.S for i in range(wl.S_max // wl.S)]
+    nb = len(starts)
+    q4, kn4, vn4 = (t.repeat(nb, 1, 1, 1).contiguous() for t in (q, kn, vn))
+    kc4, vc4 = (t.repeat(nb, 1, 1, 1).contiguous() for t in (kc, vc))
+    out4 = torch.empty_like(q4)
+    p0 = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    ws4 = torch.empty(lib.prefill_workspace_bytes(nb, wl.Hkv, max(starts) + wl.S, wl.D), dtype=torch.uint8,
+                      device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] timing chunk prefill with starts {starts}: warmup {warmup}, steps {steps}")
+    ms_v = time_calls(lambda: lib.prefill_chunk_varpos(q4, kn4, vn4, kc4, vc4, p0, max(starts), tab, out=out4,
+                                                       workspace=ws4), steps, warmup, heat=True)
+    flops_v = sum(4.0 * wl.Hq * wl.D * (p * wl.S + wl.S * wl.S / 2.0) for p in starts)
+    tf_v = flops_v / (ms_v * 1e-3) / 1e12
+    log(f"[bench] chunk prefill, starts per sequence: {ms_v:.4f} ms/step, {tf_v:.1f} TFLOP/s")
+    return {"c": c, "ms": ms, "tflops": tf, "ms_paged": ms_p, "tflops_paged": tf_p, "ms_varpos": ms_v,
+            "tflops_varpos": tf_v, "starts": starts, "flops_varpos": flops_v}
 
 
 def cpu_threads():
@@ -568,6 +590,12 @@ def main():
             "config": {"workload": "chunked prefill into a paged KV cache (16-token blocks, shuffled)", "B": wl.B,
                        "Hq": wl.Hq, "Hkv": wl.Hkv, "chunk_len": wl.S, "pos0": wl.pos0, "block_size": 16,
                        "head_dim": wl.D, "flops_per_step": wl.chunk_flops()}}
+        out["varpos_chunk_prefill"] = {
+            "value": round(r["tflops_varpos"], 2), "unit": "TFLOP/s", "ms_per_step": round(r["ms_varpos"], 5),
+            "frac": round(r["tflops_varpos"] / MFMA_BF16_PEAK_TFLOPS, 4),
+            "config": {"workload": "chunked prefill with a chunk start per sequence (attn_prefill_chunk_varpos)",
+                       "B": len(r["starts"]), "starts": r["starts"], "Hq": wl.Hq, "Hkv": wl.Hkv, "chunk_len": wl.S,
+                       "S_max": wl.S_max, "head_dim": wl.D, "flops_per_step": r["flops_varpos"]}}
     if not args.no_cpu_baseline:
         if "prefill" in res:
             log("[bench] timing the fp64 oracle on the host (cpu_baseline, prefill sample)")
