@@ -71,7 +71,7 @@ typedef enum {
 
 /* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
  * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys; 2.1.0:
- * attn_checked_sites; 2.2.0: attn_prefill_chunk_varpos. */
+ * attn_checked_sites; 2.2.0: attn_prefill_chunk_varpos and attn_prefill_chunk_paged_varpos. */
 int attn_version(void);
 
 /* Index checks of a checked build (the library compiled with ATTN_CHECKED; a debugging aid, not
@@ -304,6 +304,33 @@ attn_status attn_prefill_chunk_paged(const void* q, const void* k_new, const voi
                                      attn_dtype out_dt, int B, int Hq, int Hkv, int Sq, int D, int pos0,
                                      int window, const float* rope_table, int table_max_pos,
                                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_prefill_chunk_paged_varpos: attn_prefill_chunk_paged with a chunk start per sequence,
+ * as attn_prefill_chunk_varpos does for a contiguous cache (same page sections): sequence b's
+ * chunk goes to tokens p_b .. p_b+Sq-1, p_b = pos0[b], and its queries attend to its tokens
+ * j <= p_b + i (and, with a window W >= 0, j >= p_b + i - W; tokens before p_b - W are never
+ * read, so blocks holding only such tokens may already have been released).
+ *
+ * pos0: device int32 [B], 4-byte aligned, read on the device only; each value must lie in
+ *   [0, pos0_max].  A sequence whose value lies outside gets NaN output rows (and NaN LSE),
+ *   and none of its slots is written.
+ * pos0_max: host int >= 0: pos0_max + Sq <= max_blocks * block_size, and with RoPE
+ *   pos0_max + Sq <= table_max_pos.
+ * workspace: required, at least attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0_max, Sq, D)
+ *   bytes, 16-byte aligned, contents irrelevant.
+ * With every pos0[b] equal to p the result is attn_prefill_chunk_paged's with pos0 = p, bit for
+ * bit.  Other arguments, layouts, the support matrix and the errors as in
+ * attn_prefill_chunk_paged (with pos0_max in place of pos0); also ATTN_ERR_INVALID_ARG for a
+ * null or misaligned pos0.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_prefill_chunk_paged_varpos(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                            void* v_pages, int num_blocks, int block_size,
+                                            const int32_t* block_table, int max_blocks, const int32_t* pos0,
+                                            int pos0_max, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
+                                            int Hkv, int Sq, int D, int window, const float* rope_table,
+                                            int table_max_pos, void* workspace, size_t workspace_bytes,
+                                            void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV

@@ -277,6 +277,37 @@ def test_prefill_chunk_paged_rejects(kw, code):
     assert _chunk_paged(**kw) == code
 
 
+def _chunk_paged_varpos(**kw):
+    a = dict(q=A, kn=A, vn=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=20, p0=A, p0max=50, o=A, lse=None,
+             out_dt=BF16, B=2, Hq=8, Hkv=2, Sq=100, D=128, window=-1, table=A, tmax=300, ws=A, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = lib.prefill_chunk_paged_workspace_bytes(a["B"], a["Hkv"], max(a["p0max"], 0), a["Sq"], a["D"])
+    return lib.raw().attn_prefill_chunk_paged_varpos(a["q"], a["kn"], a["vn"], a["kp"], a["vp"], a["nblk"], a["bs"],
+                                                     a["bt"], a["mb"], a["p0"], a["p0max"], a["o"], a["lse"],
+                                                     a["out_dt"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["D"],
+                                                     a["window"], a["table"], a["tmax"], a["ws"], a["wsb"],
+                                                     a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INV), (dict(kn=None), INV), (dict(vn=None), INV), (dict(kp=None), INV), (dict(vp=None), INV),
+    (dict(bt=None), INV), (dict(o=None), INV), (dict(ws=None), INV), (dict(table=None, ws=None), INV),
+    (dict(p0=None), INV), (dict(p0=P(0x10002)), INV),
+    (dict(B=0), INV), (dict(Hq=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(D=0), INV),
+    (dict(p0max=-1), INV), (dict(Hq=8, Hkv=3), INV), (dict(nblk=0), INV), (dict(mb=0), INV),
+    (dict(bs=8), INV), (dict(bs=24), INV), (dict(bs=8192), INV),
+    (dict(mb=9), INV),                                       # pos0_max + Sq > max_blocks * block_size
+    (dict(tmax=149), INV),                                   # table too short for the last allowed position
+    (dict(wsb=lib.prefill_chunk_paged_workspace_bytes(2, 2, 50, 100, 128) - 1), INV), (dict(ws=MIS), INV),
+    (dict(q=MIS), INV), (dict(kp=MIS), INV), (dict(vn=MIS), INV), (dict(lse=MIS), INV),
+    (dict(bt=P(0x10002)), INV), (dict(table=MIS), INV), (dict(D=65), INV), (dict(out_dt=5), INV),
+    (dict(D=96, wsb=1 << 30), UNSUP), (dict(D=256, wsb=1 << 30), UNSUP),
+])
+def test_prefill_chunk_paged_varpos_rejects(kw, code):
+    assert _chunk_paged_varpos(**kw) == code
+
+
 def _paged(**kw):
     a = dict(q=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=64, cl=A, qp=A, o=A, lse=None, in_dt=BF16, out_dt=BF16,
              B=4, Hq=16, Hkv=2, D=128, window=-1, table=A, tmax=2000, ns=0, ws=A, wsb=None, stream=None)

@@ -9,7 +9,10 @@ What is checked, on seeded inputs (inputs.make_chunk draws the chunk and the who
     cache rows outside each sequence's chunk are untouched, bit for bit, and the appended rows
     match the oracle's bf16-rounded rotation;
   * starts outside [0, pos0_max]: those sequences get NaN output rows and LSE and keep their
-    cache bit for bit, while the other sequences of the batch still match the oracle.
+    cache bit for bit, while the other sequences of the batch still match the oracle;
+  * into a shuffled block pool (attn_prefill_chunk_paged_varpos): the same outputs as the
+    contiguous call bit for bit and the same cache contents in table order, each valid sequence
+    against the oracle; with equal starts, attn_prefill_chunk_paged's result bit for bit.
 """
 
 import numpy as np
@@ -132,3 +135,75 @@ def test_starts_out_of_range(lib):
         for b in (0, 3):
             _check_sequence(c, b, starts[b], o, lse, kc, vc, rope=True, window=None,
                             what=f"seq {b} (start {starts[b]}, {out_dtype})")
+
+
+def _gather_bits(pool_bits, table, bs, S):
+    """Contiguous [B, Hkv, S, D] view of a pool's slots in table order."""
+    B, nb = table.shape
+    blocks = pool_bits[table.ravel()]                      # [B*nb, Hkv, bs, D]
+    Hkv, D = blocks.shape[1], blocks.shape[3]
+    seq = blocks.reshape(B, nb, Hkv, bs, D).transpose(0, 2, 1, 3, 4).reshape(B, Hkv, nb * bs, D)
+    return seq[:, :, :S]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,Sq,S_max,D,bs,starts,pos0_max,window,rope", [
+    (4, 8, 2, 70, 420, 128, 16, [0, 37, 200, 350], 350, None, True),
+    (3, 4, 4, 129, 400, 64, 32, [5, 271, 64], 271, 90, True),
+    (2, 8, 2, 64, 256, 128, 16, [64, 0], 192, None, False),
+    (4, 8, 2, 50, 200, 128, 16, [10, -1, 151, 100], 150, None, True),    # two starts out of range
+])
+def test_paged_varpos_equals_contiguous_varpos(lib, B, Hq, Hkv, Sq, S_max, D, bs, starts, pos0_max, window, rope):
+    """The same ragged chunk into a shuffled block pool (attn_prefill_chunk_paged_varpos) and into the
+    contiguous cache (attn_prefill_chunk_varpos): outputs and LSE equal bit for bit (NaN rows
+    included), and the pool's slots, read in table order, equal the contiguous cache."""
+    banner(f"paged varpos == contiguous varpos: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} D={D} bs={bs} starts={starts} "
+           f"pos0_max={pos0_max} window={window} rope={rope}")
+    wl = inputs.Workload("v", B=B, Hq=Hq, Hkv=Hkv, S=Sq, D=D, dtype="bf16", seed=11 * Sq + bs, kind="chunk",
+                         pos0=0, S_max=S_max)
+    pc = inputs.make_paged_chunk(wl, block_size=bs)
+    c = pc.chunk
+    o, lse, kc, vc = _varpos(lib, c, starts, pos0_max, rope=rope, window=window, out_dtype=torch.float32)
+    tab = lib.make_rope_table(S_max, D) if rope else None
+    kp, vp = pc.k_pages.torch("cuda"), pc.v_pages.torch("cuda")
+    bt = torch.from_numpy(pc.block_table).cuda()
+    p0 = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    lp = torch.empty_like(lse)
+    op = lib.prefill_chunk_paged_varpos(c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda"), kp, vp, bt,
+                                        p0, pos0_max, tab, window=window, out_dtype=torch.float32, lse=lp)
+    torch.cuda.synchronize()
+    same_o = torch.equal(torch.nan_to_num(op, nan=7.0), torch.nan_to_num(o, nan=7.0))
+    same_l = torch.equal(torch.nan_to_num(lp, nan=7.0), torch.nan_to_num(lse, nan=7.0))
+    assert same_o and torch.equal(torch.isnan(op), torch.isnan(o)), "paged and contiguous outputs differ"
+    assert same_l and torch.equal(torch.isnan(lp), torch.isnan(lse)), "paged and contiguous LSE differ"
+    gk = _gather_bits(kp.cpu().view(torch.int16).numpy(), pc.block_table, bs, S_max)
+    gv = _gather_bits(vp.cpu().view(torch.int16).numpy(), pc.block_table, bs, S_max)
+    assert np.array_equal(gk, _bits(kc)), "pool keys differ from the contiguous cache"
+    assert np.array_equal(gv, _bits(vc)), "pool values differ from the contiguous cache"
+    for b, p in enumerate(starts):
+        if 0 <= p <= pos0_max:
+            _check_sequence(c, b, p, op, lp, kc, vc, rope=rope, window=window, what=f"paged seq {b} (start {p})")
+        else:
+            assert torch.isnan(op[b]).all() and torch.isnan(lp[b]).all(), f"seq {b}: not NaN"
+
+
+def test_paged_varpos_equal_starts_match_paged_chunk(lib):
+    B, Hq, Hkv, Sq, S_max, D, bs, p, pos0_max = 2, 8, 2, 77, 300, 128, 16, 100, 150
+    banner(f"paged varpos == paged chunk at equal starts p={p} (pos0_max={pos0_max})")
+    wl = inputs.Workload("v", B=B, Hq=Hq, Hkv=Hkv, S=Sq, D=D, dtype="bf16", seed=123, kind="chunk", pos0=0,
+                         S_max=S_max)
+    pc = inputs.make_paged_chunk(wl, block_size=bs)
+    c = pc.chunk
+    tab = lib.make_rope_table(S_max, D)
+    bt = torch.from_numpy(pc.block_table).cuda()
+    q, kn, vn = c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda")
+    kp1, vp1 = pc.k_pages.torch("cuda"), pc.v_pages.torch("cuda")
+    kp2, vp2 = pc.k_pages.torch("cuda"), pc.v_pages.torch("cuda")
+    l1 = torch.empty((B, Hq, Sq), dtype=torch.float32, device="cuda")
+    l2 = torch.empty_like(l1)
+    o1 = lib.prefill_chunk_paged_varpos(q, kn, vn, kp1, vp1, bt, torch.full((B,), p, dtype=torch.int32, device="cuda"),
+                                        pos0_max, tab, lse=l1)
+    o2 = lib.prefill_chunk_paged(q, kn, vn, kp2, vp2, bt, p, tab, lse=l2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2), "outputs differ"
+    assert torch.equal(kp1.view(torch.int16), kp2.view(torch.int16)) and \
+        torch.equal(vp1.view(torch.int16), vp2.view(torch.int16)), "pools differ"

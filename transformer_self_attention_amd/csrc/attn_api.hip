@@ -444,6 +444,60 @@ attn_status attn_prefill_chunk_paged(const void* q, const void* k_new, const voi
   return from_hip(attn::launch_prefill_cache(a, st));
 }
 
+attn_status attn_prefill_chunk_paged_varpos(const void* q, const void* k_new, const void* v_new, void* k_pages,
+                                            void* v_pages, int num_blocks, int block_size,
+                                            const int32_t* block_table, int max_blocks, const int32_t* pos0,
+                                            int pos0_max, void* o, float* lse, attn_dtype out_dt, int B, int Hq,
+                                            int Hkv, int Sq, int D, int window, const float* rope_table,
+                                            int table_max_pos, void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (!q || !k_new || !v_new || !k_pages || !v_pages || !block_table || !pos0 || !o || !workspace)
+    return ATTN_ERR_INVALID_ARG;
+  if (!valid_dtype(out_dt)) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || D < 1 || pos0_max < 0 || num_blocks < 1 || max_blocks < 1)
+    return ATTN_ERR_INVALID_ARG;
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks * block_size > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)pos0_max + Sq > (int64_t)max_blocks * block_size) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      !aligned16(o) || !aligned16(workspace) || (lse && !aligned16(lse)) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(pos0) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (check_rope(rope_table, table_max_pos, pos0_max, Sq) != ATTN_OK) return ATTN_ERR_INVALID_ARG;
+  if (workspace_bytes < attn_prefill_chunk_paged_workspace_bytes(B, Hkv, pos0_max, Sq, D))
+    return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hq * Sq > (int64_t)INT32_MAX / 2) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * Hkv * block_size * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+
+  hipStream_t st = (hipStream_t)stream;
+  const int Sk_max = pos0_max + Sq;
+  void* k_ws = workspace;
+  void* v_ws = static_cast<char*>(workspace) + attn::prefill_workspace_bytes(B, Hkv, Sk_max, D);
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < block_size) ++bs_log2;
+  const int kw = kernel_window(window);
+  // each sequence's start is read on the device; its rows are gathered from its own window start
+  const hipError_t e = attn::launch_cache_append_paged_varpos(k_new, v_new, k_pages, v_pages, block_table,
+                                                              max_blocks, bs_log2, num_blocks, k_ws, v_ws, B, Hkv,
+                                                              Sq, D, pos0_max, pos0, kw, rope_table, st);
+  if (e != hipSuccess) return ATTN_ERR_HIP;
+  attn::PrefillArgs a;
+  a.q = q; a.k = k_ws; a.v = v_ws; a.o = o; a.lse = lse;
+  a.out_bf16 = out_dt == ATTN_BF16;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.S = Sq; a.D = D;
+  a.causal = true;
+  a.pos0 = pos0_max;
+  a.table = rope_table;
+  a.workspace = nullptr;
+  a.Sk = Sk_max; a.k_rows = Sk_max; a.v_rows = Sk_max; a.coff = pos0_max;
+  a.window = kw;
+  a.pos0_dev = pos0;
+  return from_hip(attn::launch_prefill_cache(a, st));
+}
+
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {
   (void)D;
   if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || S_max < 1 || n_split < 0) return 0;

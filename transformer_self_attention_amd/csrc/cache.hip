@@ -138,24 +138,39 @@ hipError_t append_go(const void* k_new, const void* v_new, void* k_cache, void* 
   return hipGetLastError();
 }
 
-template <int D, bool ROPE>
+// VARPOS: chunks at per-sequence positions, as in cache_append_kernel: the grid covers rows
+// [0, pos0 + Sq) of every (batch, KV head) (pos0: the largest start allowed, and the row count
+// of the workspace copies), and sequence b, whose chunk starts at p = pos0_dev[b], writes its
+// rows from its own conv_first (the tile of p - window; zeros before p - window) to p + Sq.  A
+// sequence whose p lies outside [0, pos0] is left untouched.
+template <int D, bool ROPE, bool VARPOS>
 __global__ __launch_bounds__(256) void cache_append_paged_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_pages,
     uint16_t* __restrict__ v_pages, const int32_t* __restrict__ block_table, int max_blocks, int bs_log2,
     int num_blocks, uint16_t* __restrict__ k_ws, uint8_t* __restrict__ kexp, uint16_t* __restrict__ v_ws, int B,
-    int Hkv, int Sq, int pos0, int conv_first, int first_seen, const float2* __restrict__ table) {
+    int Hkv, int Sq, int pos0_in, int conv_first, int first_seen_in, const float2* __restrict__ table,
+    const int32_t* __restrict__ pos0_dev, int window) {
   constexpr int NCH = D / 8;  // 16-byte chunks per row
-  const int Sk = pos0 + Sq;
-  const int nrows = Sk - conv_first;
+  const int Sk = pos0_in + Sq;  // rows per (batch, KV head) of the workspace copies
+  const int first = VARPOS ? 0 : conv_first;
+  const int nrows = Sk - first;
   const int64_t n = (int64_t)B * Hkv * nrows * NCH;
   for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
        idx += (int64_t)gridDim.x * blockDim.x) {
     const int cc = (int)(idx % NCH);
     const int64_t rr = idx / NCH;
-    const int s = conv_first + (int)(rr % nrows);
+    const int s = first + (int)(rr % nrows);
     const int64_t bh = rr / nrows;
     const int b = (int)(bh / Hkv), hkv = (int)(bh % Hkv);
     const int64_t wrow = (bh * Sk + s) * D + cc * 8;  // element offset in the workspace copies
+    int pos0 = pos0_in, first_seen = first_seen_in;
+    if constexpr (VARPOS) {
+      // the NCH lanes of a row share s and b, so they skip together (to_f16_row needs all of them)
+      pos0 = pos0_dev[b];
+      if (pos0 < 0 || pos0 > pos0_in) continue;
+      first_seen = window >= pos0 ? 0 : pos0 - window;
+      if (s < (first_seen / 64) * 64 || s >= pos0 + Sq) continue;
+    }
     // checked build, site 1: the row in the workspace copies, and its table entry
     if (!ATTN_IN(b < B && s >= 0 && s < Sk && (s >> bs_log2) < max_blocks, 1)) continue;
     if (s < first_seen) {
@@ -210,12 +225,12 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
   }
 }
 
-template <int D>
+template <int D, bool VARPOS>
 hipError_t append_paged_go(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
                            const int32_t* block_table, int max_blocks, int bs_log2, int num_blocks, void* k_ws,
                            void* v_ws, int B, int Hkv, int Sq, int pos0, int conv_first, int first_seen,
-                           const float* table, hipStream_t st) {
-  const int64_t n = (int64_t)B * Hkv * (pos0 + Sq - conv_first) * (D / 8);
+                           const float* table, const int32_t* pos0_dev, int window, hipStream_t st) {
+  const int64_t n = (int64_t)B * Hkv * (pos0 + Sq - (VARPOS ? 0 : conv_first)) * (D / 8);
   int64_t blocks = (n + 255) / 256;
   if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 workgroups per CU
   if (blocks < 1) blocks = 1;
@@ -224,10 +239,11 @@ hipError_t append_paged_go(const void* k_new, const void* v_new, void* k_pages, 
                        (const uint16_t*)v_new, (uint16_t*)k_pages, (uint16_t*)v_pages, block_table, max_blocks,
                        bs_log2, num_blocks, (uint16_t*)k_ws,
                        static_cast<uint8_t*>(k_ws) + prefill_kexp_offset(B, Hkv, pos0 + Sq, D), (uint16_t*)v_ws,
-                       B, Hkv, Sq, pos0, conv_first, first_seen, reinterpret_cast<const float2*>(table));
+                       B, Hkv, Sq, pos0, conv_first, first_seen, reinterpret_cast<const float2*>(table), pos0_dev,
+                       window);
     return hipGetLastError();
   };
-  return table ? go(cache_append_paged_kernel<D, true>) : go(cache_append_paged_kernel<D, false>);
+  return table ? go(cache_append_paged_kernel<D, true, VARPOS>) : go(cache_append_paged_kernel<D, false, VARPOS>);
 }
 
 }  // namespace
@@ -238,11 +254,25 @@ hipError_t launch_cache_append_paged(const void* k_new, const void* v_new, void*
                                      const int32_t* block_table, int max_blocks, int bs_log2, int num_blocks,
                                      void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D, int pos0,
                                      int conv_first, int first_seen, const float* table, hipStream_t st) {
-  return D == 64 ? append_paged_go<64>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
-                                       num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0, conv_first, first_seen, table, st)
-                 : append_paged_go<128>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
-                                        num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0, conv_first, first_seen, table,
-                                        st);
+  return D == 64 ? append_paged_go<64, false>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
+                                              num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0, conv_first, first_seen,
+                                              table, nullptr, 0, st)
+                 : append_paged_go<128, false>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
+                                               num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0, conv_first, first_seen,
+                                               table, nullptr, 0, st);
+}
+
+hipError_t launch_cache_append_paged_varpos(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                            const int32_t* block_table, int max_blocks, int bs_log2,
+                                            int num_blocks, void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D,
+                                            int pos0_max, const int32_t* pos0_dev, int window, const float* table,
+                                            hipStream_t st) {
+  return D == 64 ? append_paged_go<64, true>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
+                                             num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0_max, 0, 0, table, pos0_dev,
+                                             window, st)
+                 : append_paged_go<128, true>(k_new, v_new, k_pages, v_pages, block_table, max_blocks, bs_log2,
+                                              num_blocks, k_ws, v_ws, B, Hkv, Sq, pos0_max, 0, 0, table, pos0_dev,
+                                              window, st);
 }
 
 hipError_t launch_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,

@@ -193,6 +193,13 @@ hipError_t launch_cache_append_paged(const void* k_new, const void* v_new, void*
                                      const int32_t* block_table, int max_blocks, int bs_log2, int num_blocks,
                                      void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D, int pos0,
                                      int conv_first, int first_seen, const float* table, hipStream_t st);
+// The same with per-sequence chunk starts pos0_dev[b] in [0, pos0_max] (k_ws / v_ws hold
+// pos0_max + Sq rows per (batch, KV head); window in kernel form sets each sequence's rows).
+hipError_t launch_cache_append_paged_varpos(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                            const int32_t* block_table, int max_blocks, int bs_log2,
+                                            int num_blocks, void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D,
+                                            int pos0_max, const int32_t* pos0_dev, int window, const float* table,
+                                            hipStream_t st);
 // The attention of a chunk against the cache: a.k holds the fp16 keys (a.table != nullptr) or
 // the bf16 cache keys (no RoPE).
 hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st);

@@ -37,6 +37,7 @@ EXPORTED = (
     "attn_prefill_chunk_varpos",
     "attn_prefill_chunk_paged_workspace_bytes",
     "attn_prefill_chunk_paged",
+    "attn_prefill_chunk_paged_varpos",
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
@@ -95,6 +96,9 @@ def _load():
     lib.attn_prefill_chunk_paged.restype = i32
     lib.attn_prefill_chunk_paged.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, fp, i32, i32, i32, i32,
                                              i32, i32, i32, i32, fp, i32, vp, sz, vp]
+    lib.attn_prefill_chunk_paged_varpos.restype = i32
+    lib.attn_prefill_chunk_paged_varpos.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, vp, fp, i32,
+                                                    i32, i32, i32, i32, i32, i32, fp, i32, vp, sz, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
@@ -504,6 +508,31 @@ def prefill_chunk_paged(q, k_new, v_new, k_pages, v_pages, block_table, pos0, ta
                                          _ptr(lse), _dt(out), B, Hq, Hkv, Sq, D, pos0, _win(window), _ptr(table),
                                          tmax, _ptr(workspace), _nbytes(workspace), _stream(stream)),
            "attn_prefill_chunk_paged")
+    return out
+
+
+def prefill_chunk_paged_varpos(q, k_new, v_new, k_pages, v_pages, block_table, pos0, pos0_max, table=None, *,
+                               window=None, out=None, out_dtype=None, lse=None, workspace=None, stream=None):
+    """prefill_chunk_paged() with a chunk start per sequence: pos0 is a device int32 [B] tensor and
+    pos0_max a host bound on its values (a sequence whose start lies outside [0, pos0_max] gets
+    NaN rows and none of its slots written).  workspace: uint8 GPU tensor of
+    >= prefill_chunk_paged_workspace_bytes(B, Hkv, pos0_max, Sq, D) bytes, allocated here when None."""
+    B, Hq, Hkv, Sq, D = _chunk_inputs(q, k_new, v_new)
+    num_blocks, bs = _pool(k_pages, v_pages, Hkv, D, q.device)
+    max_blocks = _block_table(block_table, B, q.device)
+    _need(pos0, "pos0", q.device)
+    if pos0.dtype != torch.int32 or pos0.numel() != B:
+        raise ValueError(f"pos0 must be int32 [{B}]")
+    out = _out(out, (B, Hq, Sq, D), out_dtype or (out.dtype if out is not None else q.dtype), q.device)
+    _lse(lse, B * Hq * Sq, q.device)
+    tmax = _table(table, D, q.device)
+    workspace = _scratch(workspace, prefill_chunk_paged_workspace_bytes(B, Hkv, pos0_max, Sq, D), q.device, stream)
+    _check(_lib.attn_prefill_chunk_paged_varpos(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages),
+                                                num_blocks, bs, _ptr(block_table), max_blocks, _ptr(pos0),
+                                                int(pos0_max), _ptr(out), _ptr(lse), _dt(out), B, Hq, Hkv, Sq, D,
+                                                _win(window), _ptr(table), tmax, _ptr(workspace),
+                                                _nbytes(workspace), _stream(stream)),
+           "attn_prefill_chunk_paged_varpos")
     return out
 
 
