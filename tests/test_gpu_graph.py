@@ -6,8 +6,10 @@ case captures one step on preallocated buffers, then replays it several times; b
 replay new inputs are copied into the captured buffers eagerly and the stream is synchronised,
 and each replay must equal, bit for bit, the same call made eagerly on the same inputs.  Cases:
 the prefill step (key rotation into a workspace + attention), a decode split over the cache with
-its merge pass, the multi-query decode (wide kernel + merge), and a serving step against a paged
-pool (a chunk appended into its blocks and attended, then a split decode against the pool).
+its merge pass, the multi-query decode (wide kernel + merge), a serving step against a paged
+pool (a chunk appended into its blocks and attended, then a split decode against the pool), and
+a paged chunk with per-sequence starts whose starts change between replays (they are read from
+device memory, so one capture serves every step).
 """
 
 import pytest
@@ -154,3 +156,46 @@ def test_graph_serving_step_paged(lib):
         assert torch.equal(got_d, eager[3]), f"replay {i}: decode output differs from the eager call"
         assert torch.equal(kp, k_pages) and torch.equal(vp, v_pages), f"replay {i}: pools differ"
         assert torch.isfinite(got_c.float()).all() and torch.isfinite(got_d.float()).all()
+
+
+def test_graph_varpos_chunk_new_starts_each_replay(lib):
+    """A chunk append + attention with per-sequence starts (attn_prefill_chunk_paged_varpos)
+    captured once: the starts live in device memory, so each replay can take new ones.  Each
+    replay must match the eager call on the same starts, outputs and pools bit for bit."""
+    B, Hq, Hkv, D, bs, Sq, S_max, pos0_max = 3, 8, 2, 128, 16, 64, 512, 448
+    banner(f"HIP graph: paged chunk with per-sequence starts, new starts on each of 4 replays")
+    max_blocks = S_max // bs
+    num_blocks = B * max_blocks + 2
+    g0 = torch.Generator(device="cuda").manual_seed(43)
+
+    def rnd(shape, g=g0):
+        return torch.randn(shape, generator=g, device="cuda").to(torch.bfloat16)
+
+    k_pages, v_pages = rnd((num_blocks, Hkv, bs, D)), rnd((num_blocks, Hkv, bs, D))
+    perm = torch.randperm(num_blocks, generator=torch.Generator().manual_seed(6))[:B * max_blocks]
+    block_table = perm.view(B, max_blocks).to(torch.int32).cuda()
+    q, kn, vn = rnd((B, Hq, Sq, D)), rnd((B, Hkv, Sq, D)), rnd((B, Hkv, Sq, D))
+    starts = torch.tensor([0, 100, 300], dtype=torch.int32, device="cuda")
+    tab = lib.make_rope_table(S_max, D)
+    ws_bytes = lib.prefill_chunk_paged_workspace_bytes(B, Hkv, pos0_max, Sq, D)
+
+    def step(ws, o, kp, vp):
+        lib.prefill_chunk_paged_varpos(q, kn, vn, kp, vp, block_table, starts, pos0_max, tab, out=o, workspace=ws)
+
+    ws, out = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda"), torch.empty_like(q)
+    g = _capture(lambda: step(ws, out, k_pages, v_pages))
+    ws2, out2 = torch.empty_like(ws), torch.empty_like(q)
+    for i, st in enumerate(([7, 448, 33], [448, 0, 250], [64, 64, 64], [1, 200, 447])):
+        starts.copy_(torch.tensor(st, dtype=torch.int32, device="cuda"))
+        gi = torch.Generator(device="cuda").manual_seed(400 + i)
+        for t in (q, kn, vn):
+            t.copy_(rnd(t.shape, gi))
+        kp_e, vp_e = k_pages.clone(), v_pages.clone()   # the pools as the replay will find them
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        step(ws2, out2, kp_e, vp_e)
+        torch.cuda.synchronize()
+        assert torch.equal(out, out2), f"replay {i} (starts {st}): output differs from the eager call"
+        assert torch.equal(k_pages, kp_e) and torch.equal(v_pages, vp_e), f"replay {i}: pools differ"
+        assert torch.isfinite(out.float()).all()
