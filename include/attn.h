@@ -71,7 +71,8 @@ typedef enum {
 
 /* Version of this interface (major * 10000 + minor * 100 + patch).  2.0.0: the buffer of
  * attn_rotate_keys_f16 holds one exponent byte per key row after the rotated keys; 2.1.0:
- * attn_checked_sites; 2.2.0: attn_prefill_chunk_varpos and attn_prefill_chunk_paged_varpos. */
+ * attn_checked_sites; 2.2.0: attn_prefill_chunk_varpos, attn_prefill_chunk_paged_varpos,
+ * attn_cache_append and attn_cache_append_paged. */
 int attn_version(void);
 
 /* Index checks of a checked build (the library compiled with ATTN_CHECKED; a debugging aid, not
@@ -331,6 +332,35 @@ attn_status attn_prefill_chunk_paged_varpos(const void* q, const void* k_new, co
                                             int Hkv, int Sq, int D, int window, const float* rope_table,
                                             int table_max_pos, void* workspace, size_t workspace_bytes,
                                             void* stream);
+
+/* ---------------------------------------------------------------------------------------
+ * attn_cache_append, attn_cache_append_paged: write Sq new tokens of every sequence into a
+ * KV cache and nothing else -- the step before attn_decode / attn_decode_paged in a serving loop
+ * (ninaddeshpande.com, "The KV cache and the memory wall": each new token's key and value join
+ * the cache, and the token then attends to the cache including itself).
+ *
+ * k_new, v_new: bf16 [B, Hkv, Sq, D] (k_new not yet rotated).  pos: device int32 [B], 4-byte
+ * aligned: sequence b's tokens are written at positions pos[b] .. pos[b]+Sq-1; key row i is
+ * RoPE(k_new row i) at position pos[b] + i, computed in float32 and rounded to bf16 (nearest
+ * even), exactly as attn_prefill_chunk appends it; values are copied.  Nothing else is written.
+ * attn_cache_append: k_cache, v_cache bf16 [B, Hkv, S_max, D], token t of sequence b in row t.
+ * attn_cache_append_paged: the pools and block table of attn_decode_paged (token t of sequence
+ *   b in block block_table[b * max_blocks + t / block_size], slot t % block_size; entries
+ *   outside [0, num_blocks) are clamped into it).  The blocks receiving the tokens must not be
+ *   shared between sequences.
+ * A sequence whose pos[b] lies outside [0, cap - Sq] is not written, cap being the tokens the
+ * cache holds (S_max, or max_blocks * block_size) and, with RoPE, at most table_max_pos.
+ * rope_table: NULL stores the keys as given.  Errors: ATTN_ERR_INVALID_ARG for null pointers,
+ * sizes < 1, Sq larger than the cache, misalignment, a bad block size, a table shorter than Sq;
+ * ATTN_ERR_UNSUPPORTED for D outside {64, 128}.
+ * --------------------------------------------------------------------------------------- */
+attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* pos, int B, int Hkv, int Sq, int S_max, int D,
+                              const float* rope_table, int table_max_pos, void* stream);
+attn_status attn_cache_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                    int num_blocks, int block_size, const int32_t* block_table, int max_blocks,
+                                    const int32_t* pos, int B, int Hkv, int Sq, int D, const float* rope_table,
+                                    int table_max_pos, void* stream);
 
 /* ---------------------------------------------------------------------------------------
  * attn_decode: one new query per sequence against a KV cache (ninaddeshpande.com, "The KV

@@ -363,3 +363,44 @@ def test_decode_noalloc_buffer_bound():
     need = lib.decode_workspace_bytes(32, 64, 1, 8192, 128, 0)
     assert need == 32 * 64 * 8 * 130 * 4 <= lib.NOALLOC_SCRATCH_BYTES
     assert lib.decode_workspace_bytes(32, 64, 1, 8192, 128, 64) > lib.NOALLOC_SCRATCH_BYTES
+
+
+def _append(**kw):
+    a = dict(kn=A, vn=A, kc=A, vc=A, pos=A, B=2, Hkv=2, Sq=1, S_max=300, D=128, table=A, tmax=300, stream=None)
+    a.update(kw)
+    return lib.raw().attn_cache_append(a["kn"], a["vn"], a["kc"], a["vc"], a["pos"], a["B"], a["Hkv"], a["Sq"],
+                                       a["S_max"], a["D"], a["table"], a["tmax"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), INV), (dict(vn=None), INV), (dict(kc=None), INV), (dict(vc=None), INV), (dict(pos=None), INV),
+    (dict(B=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(S_max=0), INV), (dict(D=0), INV),
+    (dict(Sq=301), INV),                                     # more new tokens than the cache holds
+    (dict(D=65), INV), (dict(tmax=0), INV), (dict(Sq=4, tmax=3), INV),
+    (dict(kn=MIS), INV), (dict(kc=MIS), INV), (dict(vc=MIS), INV), (dict(pos=P(0x10002)), INV),
+    (dict(table=MIS), INV), (dict(D=96), UNSUP), (dict(D=96, table=None), UNSUP),
+])
+def test_cache_append_rejects(kw, code):
+    assert _append(**kw) == code
+
+
+def _append_paged(**kw):
+    a = dict(kn=A, vn=A, kp=A, vp=A, nblk=100, bs=16, bt=A, mb=20, pos=A, B=2, Hkv=2, Sq=1, D=128, table=A,
+             tmax=320, stream=None)
+    a.update(kw)
+    return lib.raw().attn_cache_append_paged(a["kn"], a["vn"], a["kp"], a["vp"], a["nblk"], a["bs"], a["bt"],
+                                             a["mb"], a["pos"], a["B"], a["Hkv"], a["Sq"], a["D"], a["table"],
+                                             a["tmax"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kn=None), INV), (dict(vn=None), INV), (dict(kp=None), INV), (dict(vp=None), INV), (dict(bt=None), INV),
+    (dict(pos=None), INV), (dict(B=0), INV), (dict(Hkv=0), INV), (dict(Sq=0), INV), (dict(D=0), INV),
+    (dict(nblk=0), INV), (dict(mb=0), INV), (dict(bs=8), INV), (dict(bs=24), INV), (dict(bs=8192), INV),
+    (dict(Sq=321), INV),                                     # more new tokens than max_blocks * block_size
+    (dict(D=65), INV), (dict(Sq=4, tmax=3), INV),
+    (dict(kn=MIS), INV), (dict(kp=MIS), INV), (dict(bt=P(0x10002)), INV), (dict(pos=P(0x10002)), INV),
+    (dict(table=MIS), INV), (dict(D=96), UNSUP), (dict(D=256), UNSUP),
+])
+def test_cache_append_paged_rejects(kw, code):
+    assert _append_paged(**kw) == code

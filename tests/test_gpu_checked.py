@@ -26,6 +26,7 @@ SELECTION = [
     "tests/test_gpu_parity.py::test_decode_edges",
     "tests/test_gpu_chunk.py::test_chunk_against_oracle",
     "tests/test_gpu_chunk_varpos.py",
+    "tests/test_gpu_append.py",
     "tests/test_gpu_chunk_paged.py::test_paged_chunk_against_contiguous_and_oracle",
     "tests/test_gpu_decode_wide.py::test_decode_wide_groups",
     "tests/test_gpu_decode_wide.py::test_decode_wide_paged",

@@ -4,6 +4,7 @@
 // enqueues nothing and touches no device state.
 #include "../../include/attn.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <mutex>
@@ -496,6 +497,47 @@ attn_status attn_prefill_chunk_paged_varpos(const void* q, const void* k_new, co
   a.window = kw;
   a.pos0_dev = pos0;
   return from_hip(attn::launch_prefill_cache(a, st));
+}
+
+attn_status attn_cache_append(const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* pos, int B, int Hkv, int Sq, int S_max, int D,
+                              const float* rope_table, int table_max_pos, void* stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !pos) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || Sq < 1 || S_max < 1 || D < 1 || Sq > S_max) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_cache) || !aligned16(v_cache) ||
+      (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (!aligned16(rope_table) || table_max_pos < Sq)) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)B * Hkv * S_max * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+  const int s_cap = rope_table ? std::min(S_max, table_max_pos) : S_max;
+  return from_hip(attn::launch_kv_append(k_new, v_new, k_cache, v_cache, pos, B, Hkv, Sq, D, S_max, s_cap, nullptr,
+                                         0, 0, 0, rope_table, (hipStream_t)stream));
+}
+
+attn_status attn_cache_append_paged(const void* k_new, const void* v_new, void* k_pages, void* v_pages,
+                                    int num_blocks, int block_size, const int32_t* block_table, int max_blocks,
+                                    const int32_t* pos, int B, int Hkv, int Sq, int D, const float* rope_table,
+                                    int table_max_pos, void* stream) {
+  if (!k_new || !v_new || !k_pages || !v_pages || !block_table || !pos) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || Hkv < 1 || Sq < 1 || D < 1 || num_blocks < 1 || max_blocks < 1) return ATTN_ERR_INVALID_ARG;
+  if (block_size < 16 || block_size > 4096 || (block_size & (block_size - 1)) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks * block_size > (int64_t)INT32_MAX / 2) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)Sq > (int64_t)max_blocks * block_size) return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (D & 1)) return ATTN_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new) || !aligned16(k_pages) || !aligned16(v_pages) ||
+      (reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(pos) & 3u))
+    return ATTN_ERR_INVALID_ARG;
+  if (rope_table && (!aligned16(rope_table) || table_max_pos < Sq)) return ATTN_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return ATTN_ERR_UNSUPPORTED;
+  if ((int64_t)num_blocks * Hkv * block_size * D > (int64_t)1 << 40) return ATTN_ERR_UNSUPPORTED;
+  int bs_log2 = 0;
+  while ((1 << bs_log2) < block_size) ++bs_log2;
+  const int cap = max_blocks * block_size;
+  const int s_cap = rope_table ? std::min(cap, table_max_pos) : cap;
+  return from_hip(attn::launch_kv_append(k_new, v_new, k_pages, v_pages, pos, B, Hkv, Sq, D, 0, s_cap, block_table,
+                                         max_blocks, bs_log2, num_blocks, rope_table, (hipStream_t)stream));
 }
 
 int attn_decode_num_splits(int B, int Hq, int Hkv, int S_max, int D, int n_split) {

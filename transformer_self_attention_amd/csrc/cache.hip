@@ -26,6 +26,9 @@
 // (bf16), which the attention kernel then streams as it streams a contiguous cache.  Rows before
 // first_seen (the first query's window start; no query sees them) are written as zeros instead
 // of being read, so blocks wholly before it, and their table entries, are never touched.
+//
+// Append only (kv_append_kernel): the new rows alone, at per-sequence positions, into either
+// cache layout -- the step before a decode in a serving loop.
 #include "common.h"
 
 namespace attn {
@@ -50,6 +53,23 @@ __device__ __forceinline__ int to_f16_row(const u32x4 w, u32x4& h) {
 // b's chunk starts at p = pos0_dev[b], and only its rows [p, p + Sq) (with RoPE: from its own
 // conv_first, the tile of p - window) are written.  A sequence whose p lies outside [0, pos0]
 // is left untouched.
+// One lane's 16-byte key segment (chunk cc of a row: 4 adjacent pairs) rotated in fp32 at
+// position s with the table row s and rounded to bf16 (nearest even).
+template <int D>
+__device__ __forceinline__ u32x4 rope_chunk_bf16(const u32x4 kw, const float2* __restrict__ table, int s, int cc) {
+  const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)s * (D / 2) + cc * 4);
+  const f32x4 c01 = tp[0], c23 = tp[1];
+  const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+  u32x4 kb;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const float x0 = bf16lo(kw[p]), x1 = bf16hi(kw[p]);
+    const float c = cs[2 * p], sn = cs[2 * p + 1];
+    kb[p] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
+  }
+  return kb;
+}
+
 template <int D, bool ROPE, bool VARPOS>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -93,16 +113,8 @@ __global__ __launch_bounds__(256) void cache_append_kernel(
     const u32x4 kw = *reinterpret_cast<const u32x4*>(k_new + nrow);
     const u32x4 vw = *reinterpret_cast<const u32x4*>(v_new + nrow);
     if constexpr (ROPE) {
-      const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)s * (D / 2) + cc * 4);
-      const f32x4 c01 = tp[0], c23 = tp[1];
-      const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-      u32x4 kb, kh;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float x0 = bf16lo(kw[p]), x1 = bf16hi(kw[p]);
-        const float c = cs[2 * p], sn = cs[2 * p + 1];
-        kb[p] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
-      }
+      const u32x4 kb = rope_chunk_bf16<D>(kw, table, s, cc);
+      u32x4 kh;
       const int e = to_f16_row<NCH>(kb, kh);
       *reinterpret_cast<u32x4*>(k_cache + crow) = kb;
       *reinterpret_cast<u32x4*>(k16 + (bh * Sk + s) * D + cc * 8) = kh;
@@ -202,16 +214,8 @@ __global__ __launch_bounds__(256) void cache_append_paged_kernel(
     const u32x4 kw = *reinterpret_cast<const u32x4*>(k_new + nrow);
     const u32x4 vw = *reinterpret_cast<const u32x4*>(v_new + nrow);
     if constexpr (ROPE) {
-      const f32x4* tp = reinterpret_cast<const f32x4*>(table + (int64_t)s * (D / 2) + cc * 4);
-      const f32x4 c01 = tp[0], c23 = tp[1];
-      const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-      u32x4 kb, kh;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        const float x0 = bf16lo(kw[p]), x1 = bf16hi(kw[p]);
-        const float c = cs[2 * p], sn = cs[2 * p + 1];
-        kb[p] = pack_bf16(x0 * c - x1 * sn, x0 * sn + x1 * c);
-      }
+      const u32x4 kb = rope_chunk_bf16<D>(kw, table, s, cc);
+      u32x4 kh;
       const int e = to_f16_row<NCH>(kb, kh);
       if (cc == 0) kexp[bh * Sk + s] = (uint8_t)e;
       *reinterpret_cast<u32x4*>(k_pages + prow) = kb;
@@ -244,6 +248,70 @@ hipError_t append_paged_go(const void* k_new, const void* v_new, void* k_pages, 
     return hipGetLastError();
   };
   return table ? go(cache_append_paged_kernel<D, true, VARPOS>) : go(cache_append_paged_kernel<D, false, VARPOS>);
+}
+
+// Append only (the step before attn_decode in a serving loop): Sq new rows of every (batch, KV
+// head) at per-sequence positions, sequence b's rows p .. p+Sq-1 with p = pos[b]; keys rotated in
+// fp32 at their positions and rounded to bf16, values copied.  Into the contiguous cache
+// [B*Hkv, S_max, D] or, PAGED, into the pool [num_blocks, Hkv, 1 << bs_log2, D] through the block
+// table.  A sequence with p outside [0, s_cap - Sq] (s_cap: the rows the cache and, with RoPE, the
+// table cover) is not written.
+template <int D, bool ROPE, bool PAGED>
+__global__ __launch_bounds__(256) void kv_append_kernel(
+    const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new, uint16_t* __restrict__ k_dst,
+    uint16_t* __restrict__ v_dst, const int32_t* __restrict__ pos, int64_t n_bh, int Hkv, int Sq, int S_max,
+    int s_cap, const int32_t* __restrict__ block_table, int max_blocks, int bs_log2, int num_blocks,
+    const float2* __restrict__ table) {
+  constexpr int NCH = D / 8;  // 16-byte chunks per row
+  const int64_t n = n_bh * Sq * NCH;
+  for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n;
+       idx += (int64_t)gridDim.x * blockDim.x) {
+    const int cc = (int)(idx % NCH);
+    const int64_t rr = idx / NCH;
+    const int i = (int)(rr % Sq);
+    const int64_t bh = rr / Sq;
+    const int b = (int)(bh / Hkv), hkv = (int)(bh % Hkv);
+    const int p = pos[b];
+    if (p < 0 || p > s_cap - Sq) continue;
+    const int s = p + i;
+    int64_t drow;  // element offset of the row's chunk in the cache or pool
+    if constexpr (PAGED) {
+      int blk = block_table[(int64_t)b * max_blocks + (s >> bs_log2)];
+      blk = min(max(blk, 0), num_blocks - 1);
+      drow = ((((int64_t)blk * Hkv + hkv) << bs_log2) + (s & ((1 << bs_log2) - 1))) * D + cc * 8;
+      // checked build, site 3: the slot in the pool
+      if (!ATTN_IN((s >> bs_log2) < max_blocks && drow + 8 <= ((int64_t)num_blocks * Hkv << bs_log2) * D, 3))
+        continue;
+    } else {
+      drow = (bh * S_max + s) * D + cc * 8;
+      // checked build, site 4: the row in the cache
+      if (!ATTN_IN(s < S_max, 4)) continue;
+    }
+    const int64_t nrow = (bh * Sq + i) * D + cc * 8;  // element offset in the new rows
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(k_new + nrow);
+    const u32x4 vw = *reinterpret_cast<const u32x4*>(v_new + nrow);
+    *reinterpret_cast<u32x4*>(k_dst + drow) = ROPE ? rope_chunk_bf16<D>(kw, table, s, cc) : kw;
+    *reinterpret_cast<u32x4*>(v_dst + drow) = vw;
+  }
+}
+
+template <int D>
+hipError_t kv_append_go(const void* k_new, const void* v_new, void* k_dst, void* v_dst, const int32_t* pos, int B,
+                        int Hkv, int Sq, int S_max, int s_cap, const int32_t* block_table, int max_blocks,
+                        int bs_log2, int num_blocks, const float* table, hipStream_t st) {
+  const int64_t n_bh = (int64_t)B * Hkv;
+  int64_t blocks = (n_bh * Sq * (D / 8) + 255) / 256;
+  if (blocks > 8192) blocks = 8192;  // grid-stride beyond ~32 workgroups per CU
+  if (blocks < 1) blocks = 1;
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(256), 0, st, (const uint16_t*)k_new,
+                       (const uint16_t*)v_new, (uint16_t*)k_dst, (uint16_t*)v_dst, pos, n_bh, Hkv, Sq, S_max, s_cap,
+                       block_table, max_blocks, bs_log2, num_blocks, reinterpret_cast<const float2*>(table));
+    return hipGetLastError();
+  };
+  if (block_table)
+    return table ? go(kv_append_kernel<D, true, true>) : go(kv_append_kernel<D, false, true>);
+  return table ? go(kv_append_kernel<D, true, false>) : go(kv_append_kernel<D, false, false>);
 }
 
 }  // namespace
@@ -291,6 +359,15 @@ hipError_t launch_cache_append_varpos(const void* k_new, const void* v_new, void
                                        table, pos0_dev, window, st)
                  : append_go<128, true>(k_new, v_new, k_cache, v_cache, k16, B, Hkv, Sq, S_max, pos0_max, 0,
                                         table, pos0_dev, window, st);
+}
+
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_dst, void* v_dst, const int32_t* pos,
+                            int B, int Hkv, int Sq, int D, int S_max, int s_cap, const int32_t* block_table,
+                            int max_blocks, int bs_log2, int num_blocks, const float* table, hipStream_t st) {
+  return D == 64 ? kv_append_go<64>(k_new, v_new, k_dst, v_dst, pos, B, Hkv, Sq, S_max, s_cap, block_table,
+                                    max_blocks, bs_log2, num_blocks, table, st)
+                 : kv_append_go<128>(k_new, v_new, k_dst, v_dst, pos, B, Hkv, Sq, S_max, s_cap, block_table,
+                                     max_blocks, bs_log2, num_blocks, table, st);
 }
 
 }  // namespace attn

@@ -200,6 +200,13 @@ hipError_t launch_cache_append_paged_varpos(const void* k_new, const void* v_new
                                             int num_blocks, void* k_ws, void* v_ws, int B, int Hkv, int Sq, int D,
                                             int pos0_max, const int32_t* pos0_dev, int window, const float* table,
                                             hipStream_t st);
+// Append only: Sq new rows per (batch, KV head) at per-sequence positions pos[b] (device int32
+// [B]) into the contiguous cache [B*Hkv, S_max, D] (block_table == nullptr) or the pool
+// [num_blocks, Hkv, 1 << bs_log2, D]; keys rotated when table != nullptr.  Sequences with a
+// position outside [0, s_cap - Sq] are not written.
+hipError_t launch_kv_append(const void* k_new, const void* v_new, void* k_dst, void* v_dst, const int32_t* pos,
+                            int B, int Hkv, int Sq, int D, int S_max, int s_cap, const int32_t* block_table,
+                            int max_blocks, int bs_log2, int num_blocks, const float* table, hipStream_t st);
 // The attention of a chunk against the cache: a.k holds the fp16 keys (a.table != nullptr) or
 // the bf16 cache keys (no RoPE).
 hipError_t launch_prefill_cache(const PrefillArgs& a, hipStream_t st);

@@ -38,6 +38,8 @@ EXPORTED = (
     "attn_prefill_chunk_paged_workspace_bytes",
     "attn_prefill_chunk_paged",
     "attn_prefill_chunk_paged_varpos",
+    "attn_cache_append",
+    "attn_cache_append_paged",
     "attn_decode_workspace_bytes",
     "attn_decode_num_splits",
     "attn_decode",
@@ -99,6 +101,10 @@ def _load():
     lib.attn_prefill_chunk_paged_varpos.restype = i32
     lib.attn_prefill_chunk_paged_varpos.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, vp, fp, i32,
                                                     i32, i32, i32, i32, i32, i32, fp, i32, vp, sz, vp]
+    lib.attn_cache_append.restype = i32
+    lib.attn_cache_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, fp, i32, vp]
+    lib.attn_cache_append_paged.restype = i32
+    lib.attn_cache_append_paged.argtypes = [vp, vp, vp, vp, i32, i32, vp, i32, vp, i32, i32, i32, i32, fp, i32, vp]
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.attn_decode_num_splits.restype = i32
@@ -534,6 +540,53 @@ def prefill_chunk_paged_varpos(q, k_new, v_new, k_pages, v_pages, block_table, p
                                                 _nbytes(workspace), _stream(stream)),
            "attn_prefill_chunk_paged_varpos")
     return out
+
+
+def _append_inputs(k_new, v_new, pos):
+    """Shapes of an append's k_new, v_new [B, Hkv, Sq, D] (bf16) and its int32 [B] positions."""
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n)
+        if t.dtype != torch.bfloat16 or t.dim() != 4:
+            raise ValueError(f"{n} must be bfloat16 [B, Hkv, Sq, D]")
+    if v_new.shape != k_new.shape or v_new.device != k_new.device:
+        raise ValueError("v_new must match k_new")
+    B, Hkv, Sq, D = k_new.shape
+    _need(pos, "pos", k_new.device)
+    if pos.dtype != torch.int32 or pos.numel() != B:
+        raise ValueError(f"pos must be int32 [{B}]")
+    return B, Hkv, Sq, D
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, pos, table=None, *, stream=None):
+    """Write Sq new tokens of every sequence into the cache [B, Hkv, S_max, D] (bf16): sequence b's
+    at rows pos[b] .. pos[b]+Sq-1 (pos: device int32 [B]), keys rotated there, values copied; a
+    sequence whose rows would leave the cache (or the table) is not written."""
+    B, Hkv, Sq, D = _append_inputs(k_new, v_new, pos)
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B, Hkv, S_max, D]")
+    S_max = k_cache.shape[2]
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, k_new.device)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{n} must be bfloat16")
+        _shape(t, (B, Hkv, S_max, D), n)
+    tmax = _table(table, D, k_new.device)
+    _check(_lib.attn_cache_append(_ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache), _ptr(pos), B, Hkv, Sq,
+                                  S_max, D, _ptr(table), tmax, _stream(stream)),
+           "attn_cache_append")
+
+
+def cache_append_paged(k_new, v_new, k_pages, v_pages, block_table, pos, table=None, *, stream=None):
+    """cache_append() into a paged pool [num_blocks, Hkv, block_size, D] with an int32 block table
+    [B, max_blocks] (token t of sequence b in block block_table[b, t // block_size])."""
+    B, Hkv, Sq, D = _append_inputs(k_new, v_new, pos)
+    num_blocks, bs = _pool(k_pages, v_pages, Hkv, D, k_new.device)
+    max_blocks = _block_table(block_table, B, k_new.device)
+    tmax = _table(table, D, k_new.device)
+    _check(_lib.attn_cache_append_paged(_ptr(k_new), _ptr(v_new), _ptr(k_pages), _ptr(v_pages), num_blocks, bs,
+                                        _ptr(block_table), max_blocks, _ptr(pos), B, Hkv, Sq, D, _ptr(table), tmax,
+                                        _stream(stream)),
+           "attn_cache_append_paged")
 
 
 def decode_workspace_bytes(B, Hq, Hkv, S_max, D, n_split=0) -> int:
