@@ -10,7 +10,8 @@ One step = one pass of the hot path over the workload's synthetic batch:
     same two kernels (a GPU test checks that both routes give identical bytes).
   * decode (sub-object ``decode``): batch 32 against an 8192-token cache, Hq=64, Hkv=8, D=128,
     query rotated at position 8192; one attn_decode call (for this shape one launch: a workgroup
-    per (sequence, KV head) streams the whole cache).
+    per (sequence, KV head) streams the whole cache).  Side figure ``ms_per_step_with_append``:
+    the serving-loop step, attn_cache_append of each sequence's new token, then the decode.
   * MHA (sub-object ``mha_prefill``): B=4, H=32, S=2048, D=128 prefill, same step.
   * long (sub-object ``long_prefill``, skipped with --no-long): the 32k-token prefill with 1% of
     key rows scaled by 8, written as fp32 output (the output held to the parity bars there).
@@ -246,7 +247,24 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
     n_split = lib.decode_num_splits(wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, 0)
-    return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
+    # the whole decode step of a serving loop: append each sequence's new key and value (at the
+    # last cache row here, the cache being full) and attend to the cache including them
+    k1 = torch.empty((wl.B, wl.Hkv, 1, wl.D), dtype=kc.dtype, device="cuda").normal_()
+    v1 = torch.empty_like(k1).normal_()
+    last = torch.full((wl.B,), wl.S - 1, dtype=torch.int32, device="cuda")
+    kc2, vc2 = kc.clone(), vc.clone()
+    tab2 = lib.make_rope_table(wl.S, wl.D)
+    torch.cuda.synchronize()
+
+    def step():
+        lib.cache_append(k1, v1, kc2, vc2, last, tab2)
+        lib.decode(q, kc2, vc2, cl, last, tab2, window=W, out=out, workspace=ws)
+
+    ms_app = time_calls(step, steps, warmup, heat=True)
+    del kc2, vc2
+    log(f"[bench] decode step with the append: {ms_app:.4f} ms/step")
+    return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup,
+            "ms_with_append": ms_app}
 
 
 def bench_rope(lib, p, steps, warmup):
@@ -513,7 +531,9 @@ def main():
                             "kernel": ("decode_split_kernel (whole cache per workgroup, writes o)"
                                        if r["n_split"] == 1 else "decode_split_kernel + decode_merge_kernel"),
                             "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode")}}
+                            "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic("decode")},
+               # the serving-loop step: attn_cache_append of each sequence's new token, then this decode
+               "ms_per_step_with_append": round(r["ms_with_append"], 5)}
         if "prefill" not in res:
             out.update({"value": dec["value"], "unit": "GB/s", "ms_per_step": dec["ms_per_step"],
                         "config": dec["config"], "roofline": dec["roofline"]})
