@@ -68,7 +68,7 @@ HBM_PEAK_GBS = 8000.0              # MI355X HBM3E peak
 MEASURED_TRAFFIC = {
     # prefill_bf16_kernel, pre-rotated keys, GQA B=1 Hq=64 Hkv=8 S=8192 D=128 (11 dispatches):
     # FETCH_SIZE 160747.8 KiB, WRITE_SIZE 131113.4 KiB per dispatch.
-    "prefill_gqa": {"bytes_per_launch": 463471532, "sources_sha256_16": "7636ee453828a278"},
+    "prefill_gqa": {"bytes_per_launch": 463471532, "sources_sha256_16": "189423014941fefe"},
     # decode_split_kernel (one split, writes o), B=32 L=8192 Hq=64 Hkv=8 D=128 (16 dispatches):
     # FETCH_SIZE 528498.7 KiB, WRITE_SIZE 512.0 KiB per step.
     "decode": {"bytes_per_launch": 1082889696, "sources_sha256_16": "eb68ae94593b2434"},

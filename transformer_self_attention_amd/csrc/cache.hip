@@ -48,11 +48,6 @@ __device__ __forceinline__ int to_f16_row(const u32x4 w, u32x4& h) {
   return e;
 }
 
-// VARPOS: chunks at per-sequence positions.  The grid then covers rows [0, pos0 + Sq) of every
-// (batch, KV head), pos0 being the largest start allowed and the k16 / kexp row count; sequence
-// b's chunk starts at p = pos0_dev[b], and only its rows [p, p + Sq) (with RoPE: from its own
-// conv_first, the tile of p - window) are written.  A sequence whose p lies outside [0, pos0]
-// is left untouched.
 // One lane's 16-byte key segment (chunk cc of a row: 4 adjacent pairs) rotated in fp32 at
 // position s with the table row s and rounded to bf16 (nearest even).
 template <int D>
@@ -70,6 +65,11 @@ __device__ __forceinline__ u32x4 rope_chunk_bf16(const u32x4 kw, const float2* _
   return kb;
 }
 
+// VARPOS: chunks at per-sequence positions.  The grid then covers rows [0, pos0 + Sq) of every
+// (batch, KV head), pos0 being the largest start allowed and the k16 / kexp row count; sequence
+// b's chunk starts at p = pos0_dev[b], and only its rows [p, p + Sq) (with RoPE: from its own
+// conv_first, the tile of p - window) are written.  A sequence whose p lies outside [0, pos0]
+// is left untouched.
 template <int D, bool ROPE, bool VARPOS>
 __global__ __launch_bounds__(256) void cache_append_kernel(
     const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
@@ -276,12 +276,12 @@ __global__ __launch_bounds__(256) void kv_append_kernel(
     const int s = p + i;
     int64_t drow;  // element offset of the row's chunk in the cache or pool
     if constexpr (PAGED) {
+      // checked build, site 3: the table entry, then the slot in the pool
+      if (!ATTN_IN((s >> bs_log2) < max_blocks, 3)) continue;
       int blk = block_table[(int64_t)b * max_blocks + (s >> bs_log2)];
       blk = min(max(blk, 0), num_blocks - 1);
       drow = ((((int64_t)blk * Hkv + hkv) << bs_log2) + (s & ((1 << bs_log2) - 1))) * D + cc * 8;
-      // checked build, site 3: the slot in the pool
-      if (!ATTN_IN((s >> bs_log2) < max_blocks && drow + 8 <= ((int64_t)num_blocks * Hkv << bs_log2) * D, 3))
-        continue;
+      if (!ATTN_IN(drow + 8 <= ((int64_t)num_blocks * Hkv << bs_log2) * D, 3)) continue;
     } else {
       drow = (bh * S_max + s) * D + cc * 8;
       // checked build, site 4: the row in the cache

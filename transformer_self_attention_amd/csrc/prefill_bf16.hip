@@ -123,6 +123,7 @@ void prefill_bf16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restr
   const int h = hkv * G + gq;
   int Sk = Sk_in, coff = coff_in, pos0 = pos0_in;
   if constexpr (VARPOS) {
+    if (!ATTN_IN(b < B, 0)) return;  // checked build, site 0: the sequence whose start is read
     const int p = __builtin_amdgcn_readfirstlane(pos0_dev[b]);
     if (p < 0 || p > coff_in) {
       // no valid chunk position: the workgroup's output rows (and LSE) become NaN
