@@ -224,7 +224,7 @@ def bench_prefill(lib, inputs, wl, steps, warmup, variants=True, out_dtype=None,
     return r
 
 
-def bench_decode(lib, inputs, wl, steps, warmup):
+def bench_decode(lib, inputs, wl, steps, warmup, with_append=False):
     import torch
     log(f"[bench] generating decode inputs B={wl.B} cache={wl.S} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D}")
     d = inputs.make_decode(wl)
@@ -247,6 +247,8 @@ def bench_decode(lib, inputs, wl, steps, warmup):
     gbs = nbytes / (ms * 1e-3) / 1e9
     log(f"[bench] decode: {ms:.4f} ms/step, {gbs:.1f} GB/s of K/V")
     n_split = lib.decode_num_splits(wl.B, wl.Hq, wl.Hkv, wl.S, wl.D, 0)
+    if not with_append:
+        return {"d": d, "ms": ms, "gbs": gbs, "n_split": n_split, "steps": steps, "warmup": warmup}
     # the whole decode step of a serving loop: append each sequence's new key and value (at the
     # last cache row here, the cache being full) and attend to the cache including them
     k1 = torch.empty((wl.B, wl.Hkv, 1, wl.D), dtype=kc.dtype, device="cuda").normal_()
@@ -458,7 +460,7 @@ def main():
         res["rope"] = bench_rope(lib, res["prefill"]["p"], 4 * args.steps, 4 * args.warmup)
         log(f"[bench] reference: torch bf16 GEMM 8192^3 {res['gemm_tflops']:.1f} TFLOP/s")
     if args.only in ("decode", "all"):
-        res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup)
+        res["decode"] = bench_decode(lib, inputs, W["decode"], 4 * args.steps, 4 * args.warmup, with_append=True)
     if args.only in ("mha", "all"):
         res["mha"] = bench_prefill(lib, inputs, W["mha"], args.steps, args.warmup, variants=False, heat=True)
     if args.only in ("swa", "all"):
