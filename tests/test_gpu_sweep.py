@@ -2,8 +2,9 @@
 
 Each case draws its configuration from a seeded generator (batch, heads and group size up to 64
 query heads per KV head, lengths that are not tile multiples, head dim, window, position offset,
-output dtype, key mode, split count, block size) and checks the HIP result with the bf16 bars.
-The configuration is printed before each launch.
+output dtype, key mode, split count, block size, per-sequence chunk starts, one of them sometimes
+out of range) and checks the HIP result with the bf16 bars; the per-sequence sweep also appends
+each sequence's next token and decodes it.  The configuration is printed before each launch.
 """
 
 import numpy as np
@@ -153,3 +154,67 @@ def test_paged_chunk_sweep(lib, seed):
     ck, cv = oracle.gather_pages(rk, rv, p.block_table, pos0 + Sq)
     ref, _ = oracle.attention_with_cache(c.q.f64(), ck, cv, pos0, rope_base=base, window=W)
     assert_bf16_parity(to_np(o), ref, "o")
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_varpos_chunk_sweep(lib, seed):
+    """Chunks at per-sequence starts (contiguous or paged), then one append + decode step per
+    sequence at its next position; every sequence against the oracle run on it alone."""
+    rng = np.random.default_rng(9000 + seed)
+    Hq, Hkv = _heads(rng)
+    B = int(rng.integers(1, 5))
+    Sq = int(rng.integers(1, 300))
+    S_max = Sq + int(rng.integers(1, 700))
+    pos0_max = S_max - Sq - 1          # room for the decode token after the chunk
+    starts = [int(rng.integers(0, pos0_max + 1)) for _ in range(B)]
+    if B > 1 and rng.random() < 0.3:
+        starts[int(rng.integers(0, B))] = pos0_max + 1 + int(rng.integers(0, 5))   # out of range: NaN rows
+    D = int(rng.choice([64, 128]))
+    bs = int(rng.choice([16, 32, 64]))
+    W = int(rng.integers(0, S_max)) if rng.random() < 0.4 else None
+    rope = bool(rng.random() < 0.8)
+    paged = bool(rng.random() < 0.5)
+    banner(f"varpos sweep seed={seed}: B={B} Hq={Hq} Hkv={Hkv} Sq={Sq} S_max={S_max} starts={starts} "
+           f"pos0_max={pos0_max} D={D} bs={bs} W={W} rope={rope} paged={paged}")
+    wl = inputs.Workload("v", B=B, Hq=Hq, Hkv=Hkv, S=Sq, D=D, dtype="bf16", seed=10000 + seed, kind="chunk",
+                         pos0=0, S_max=S_max)
+    pc = inputs.make_paged_chunk(wl, block_size=bs)
+    c = pc.chunk
+    tab = lib.make_rope_table(S_max, D) if rope else None
+    p0 = torch.tensor(starts, dtype=torch.int32, device="cuda")
+    q, kn, vn = c.q.torch("cuda"), c.k_new.torch("cuda"), c.v_new.torch("cuda")
+    if paged:
+        kc, vc = pc.k_pages.torch("cuda"), pc.v_pages.torch("cuda")
+        bt = torch.from_numpy(pc.block_table).cuda()
+        o = lib.prefill_chunk_paged_varpos(q, kn, vn, kc, vc, bt, p0, pos0_max, tab, window=W,
+                                           out_dtype=torch.float32)
+    else:
+        kc, vc = c.k_cache.torch("cuda"), c.v_cache.torch("cuda")
+        o = lib.prefill_chunk_varpos(q, kn, vn, kc, vc, p0, pos0_max, tab, window=W, out_dtype=torch.float32)
+    # one decode step at each valid sequence's next position: append its token, then attend
+    grng = np.random.Generator(np.random.PCG64(11000 + seed))
+    q1 = inputs.Tensor(grng.standard_normal((B, Hq, 1, D)).astype(np.float32), "bf16")
+    k1 = inputs.Tensor(grng.standard_normal((B, Hkv, 1, D)).astype(np.float32), "bf16")
+    v1 = inputs.Tensor(grng.standard_normal((B, Hkv, 1, D)).astype(np.float32), "bf16")
+    nxt = np.array([p + Sq if p <= pos0_max else 0 for p in starts], dtype=np.int32)
+    nxt_t = torch.from_numpy(nxt).cuda()
+    if paged:
+        lib.cache_append_paged(k1.torch("cuda"), v1.torch("cuda"), kc, vc, bt, nxt_t, tab)
+        od = lib.decode_paged(q1.torch("cuda"), kc, vc, bt, nxt_t + 1, nxt_t, tab, window=W, out_dtype=torch.float32)
+    else:
+        lib.cache_append(k1.torch("cuda"), v1.torch("cuda"), kc, vc, nxt_t, tab)
+        od = lib.decode(q1.torch("cuda"), kc, vc, nxt_t + 1, nxt_t, tab, window=W, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    base = 10000.0 if rope else None
+    for b, p in enumerate(starts):
+        if p > pos0_max:
+            assert torch.isnan(o[b]).all(), f"seq {b}: start {p} out of range, output not NaN"
+            continue
+        sl = slice(b, b + 1)
+        rk, rv = oracle.append_to_cache(c.k_cache.f64()[sl], c.v_cache.f64()[sl], c.k_new.f64()[sl],
+                                        c.v_new.f64()[sl], p, rope_base=base)
+        ref, _ = oracle.attention_with_cache(c.q.f64()[sl], rk, rv, p, rope_base=base, window=W)
+        assert_bf16_parity(to_np(o)[sl], ref, f"seq {b} chunk at {p}")
+        rk, rv = oracle.append_to_cache(rk, rv, k1.f64()[sl], v1.f64()[sl], p + Sq, rope_base=base)
+        ref1, _ = oracle.attention_with_cache(q1.f64()[sl], rk, rv, p + Sq, rope_base=base, window=W)
+        assert_bf16_parity(to_np(od)[sl], ref1, f"seq {b} decode at {p + Sq}")
